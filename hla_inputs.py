@@ -1,0 +1,106 @@
+"""Seeded synthetic inputs for the gated linear / gated softmax attention path.
+
+This module only draws random tensors and names workload shapes. It holds none of
+the attention arithmetic, so both the fp64 oracle (``oracle/``) and the HIP path
+(``softmax_attention_amd``) can take their inputs from it without sharing code.
+
+Shapes follow the spatio-temporal latent token sequences the SANA-Video 2.0 pages
+describe (480x832 video at 81/121/193 frames, "about 19,000 tokens" at 720p; page
+"SANA-Video 2.0 ... (ai-papers.net)", sections on hybrid linear attention and on
+experimental results). The pages publish no tensors, so every value here is
+i.i.d. N(0, 1) from a seeded CPU generator, rounded to bf16 (round to nearest even)
+for the bf16 workloads. The same rounded tensors go to the GPU and, upcast
+exactly, to the oracle.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import List, Tuple
+
+import torch
+
+SEED_BASE = 20261203
+# tensor slot inside a layer's seed: q, k, v, g, and the residual stream x0
+SLOT = {"q": 0, "k": 1, "v": 2, "g": 3, "x0": 4}
+
+LINEAR = 0
+SOFTMAX = 1
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One named workload: shape, dtype and which operators it exercises."""
+
+    index: int          # 1-based workload number; part of the seed
+    name: str
+    B: int
+    H: int
+    N: int
+    D: int
+    dtype: str          # "f32" or "bf16"
+    latent: Tuple[int, int, int]  # (T, H, W) latent grid; N = T*H*W
+    kinds: Tuple[int, ...] = (LINEAR, SOFTMAX)
+    eps: float = 1e-6
+    note: str = ""
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    @property
+    def scale(self) -> float:
+        return self.D ** -0.5
+
+
+WORKLOADS: List[Workload] = [
+    Workload(1, "tiny_f32", 1, 2, 256, 32, "f32", (4, 8, 8),
+             note="one gated linear + one gated softmax layer, fp32"),
+    Workload(2, "480p_81f", 2, 16, 8190, 128, "bf16", (21, 15, 26),
+             note="480p x 81 frames, B=2 (CFG pair)"),
+    Workload(3, "720p_81f", 2, 16, 19320, 128, "bf16", (21, 23, 40),
+             note="720p x 81 frames, B=2 (CFG pair)"),
+    Workload(4, "stack_720p_121f", 1, 16, 28520, 128, "bf16", (31, 23, 40),
+             kinds=(LINEAR, LINEAR, LINEAR, SOFTMAX, LINEAR, LINEAR, LINEAR, SOFTMAX),
+             note="3:1 hybrid stack of 8 layers, fp32 residual stream"),
+    Workload(5, "long_720p_193f", 1, 16, 45080, 128, "bf16", (49, 23, 40),
+             note="720p x 193 frames"),
+]
+
+BY_NAME = {w.name: w for w in WORKLOADS}
+
+
+def seed_for(workload_index: int, layer: int, slot: str) -> int:
+    return SEED_BASE + 1000 * workload_index + 10 * layer + SLOT[slot]
+
+
+def randn(shape, seed: int, dtype: torch.dtype) -> torch.Tensor:
+    """N(0,1) drawn in fp32 on the CPU from ``seed``, then cast (RNE) to ``dtype``."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(int(seed))
+    t = torch.randn(tuple(shape), generator=gen, dtype=torch.float32)
+    return t if dtype == torch.float32 else t.to(dtype)
+
+
+def layer_inputs(w: Workload, layer: int, B: int = None, H: int = None, N: int = None):
+    """(q, k, v, g) CPU tensors of shape [B, H, N, D] for ``layer`` of workload ``w``.
+
+    B/H/N may be overridden (smaller shapes for tests) while keeping the seeds.
+    """
+    B = w.B if B is None else B
+    H = w.H if H is None else H
+    N = w.N if N is None else N
+    shape = (B, H, N, w.D)
+    return tuple(randn(shape, seed_for(w.index, layer, s), w.torch_dtype) for s in ("q", "k", "v", "g"))
+
+
+def residual_x0(w: Workload, B: int = None, H: int = None, N: int = None) -> torch.Tensor:
+    """fp32 residual stream x0 for the hybrid stack (always fp32)."""
+    B = w.B if B is None else B
+    H = w.H if H is None else H
+    N = w.N if N is None else N
+    return randn((B, H, N, w.D), seed_for(w.index, 0, "x0"), torch.float32)
+
+
+def custom(shape, seed: int, dtype: torch.dtype = torch.float32, n: int = 4):
+    """``n`` independent N(0,1) tensors of ``shape`` from consecutive seeds."""
+    return tuple(randn(shape, seed + i, dtype) for i in range(n))

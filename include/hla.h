@@ -1,0 +1,126 @@
+/*
+ * hla.h -- C ABI of the hybrid linear-softmax attention hot path (gfx950 / MI355X).
+ *
+ * The operators are the token mixers of SANA-Video 2.0's hybrid attention: gated
+ * linear attention, which mixes tokens through a fixed-size per-head state in O(N),
+ * and a gated softmax "anchor" that keeps exact, full-rank token interactions;
+ * the two are interleaved 3:1 with a softmax anchor on every fourth layer
+ * (SANA-Video 2.0 abstract, thelatestinai.com paper listing; ai-papers.net
+ * summary, section on hybrid linear attention; lode.cx article, "How It Works").
+ * The pages give no formulas. This library computes, per batch b and head h,
+ * with rows of Q, K, V, G in R^{N x D} being tokens:
+ *
+ *   phi(x) = max(x, 0),  sigma(x) = 1 / (1 + exp(-x))
+ *   linear : S = phi(K)^T V (D x D),  z = sum_n phi(K_n) (D)
+ *            O_n = sigma(G_n) (.) (phi(Q_n) S) / (phi(Q_n) . z + eps)
+ *   softmax: O = sigma(G) (.) softmax_rows(scale * Q K^T) V   (non-causal, no mask)
+ *   stack  : x <- x + layer_l(Q_l, K_l, V_l, G_l) for l = 0 .. n_layers-1
+ *
+ * Memory layout of every tensor: [B, H, N, D], row-major and contiguous (D is the
+ * fastest dimension). q, k, v and g share dtype dims->in_dtype; the output has
+ * dims->out_dtype. All tensor and workspace pointers are DEVICE pointers owned by
+ * the caller; the library allocates nothing and keeps no pointer after a call
+ * returns. Pointer arrays and `kinds` of the stack call are HOST arrays.
+ *
+ * Supported combinations:
+ *   in_dtype HLA_F32  -> out_dtype HLA_F32                 D in {32, 64, 128}
+ *   in_dtype HLA_BF16 -> out_dtype HLA_BF16 or HLA_F32     D in {64, 128}
+ * bf16 paths multiply in bf16 on the matrix cores and accumulate in fp32; the fp32
+ * paths compute in fp32 throughout.
+ *
+ * Errors: every argument is checked on the host before any HIP call. On error
+ * nothing is enqueued and the output is untouched. On success the work is
+ * enqueued on `stream` (a hipStream_t; NULL means the null stream) and the call
+ * returns without synchronising; device faults surface at the caller's next sync.
+ * A tensor with B*H*N == 0 is empty: after the checks the call returns HLA_OK and
+ * enqueues nothing (pointers may then be NULL). Calls are reentrant; calls that
+ * share a workspace must be ordered on one stream. out/x must not overlap any
+ * input or the workspace.
+ */
+#ifndef HLA_H
+#define HLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HLA_ABI_VERSION 1
+
+typedef enum { HLA_F32 = 0, HLA_BF16 = 1 } hla_dtype;
+
+typedef enum { HLA_LAYER_LINEAR = 0, HLA_LAYER_SOFTMAX = 1 } hla_layer_kind;
+
+typedef enum {
+  HLA_OK = 0,
+  HLA_ERR_NULL_PTR = 1,    /* a required pointer is NULL */
+  HLA_ERR_BAD_SHAPE = 2,   /* a dim < 0, D <= 0, or a byte size / index overflows */
+  HLA_ERR_UNSUPPORTED = 3, /* D or dtype combination not built */
+  HLA_ERR_BAD_ARG = 4,     /* eps, scale, accumulate, n_layers or a kind out of range */
+  HLA_ERR_ALIGN = 5,       /* a tensor or workspace pointer is not 16-byte aligned */
+  HLA_ERR_WORKSPACE = 6,   /* workspace_bytes smaller than required */
+  HLA_ERR_HIP = 7          /* the HIP runtime reported an error at launch */
+} hla_status;
+
+typedef struct {
+  int64_t B, H, N, D;  /* batch, heads, tokens, head dim */
+  int32_t in_dtype;    /* hla_dtype of q, k, v, g */
+  int32_t out_dtype;   /* hla_dtype of out / x */
+} hla_dims;
+
+/* ABI version of the loaded library (HLA_ABI_VERSION it was built with). */
+int hla_abi_version(void);
+
+/* Static, NUL-terminated name of a status code ("HLA_OK", ...); "HLA_UNKNOWN"
+ * for a value outside the enum. */
+const char* hla_status_str(int status);
+
+/* Bytes of device workspace hla_linear_fwd (and the stack call) needs for `d`:
+ * per-chunk partial states B*H*C*(D*D + D) fp32 plus the reduced state in the
+ * form the output pass reads. Host-only and pure: equal dims give equal sizes.
+ * Returns 0 for invalid or unsupported dims, and for empty tensors. */
+size_t hla_linear_workspace_bytes(const hla_dims* d);
+
+/* Gated linear attention (non-causal) -- the O(N) fixed-size-state mixer of the
+ * ai-papers.net summary, section on hybrid linear attention, and of the
+ * SANA-Video 2.0 abstract. Computes O as defined above; accumulate = 0 stores
+ * out = O, accumulate = 1 updates out += O in place. eps must be finite and
+ * >= 0 (with eps = 0 a token with phi(Q_n) . z == 0 yields NaN; with eps > 0
+ * such a token yields exactly 0). `workspace` is a device buffer of at least
+ * hla_linear_workspace_bytes(d) bytes; its contents on entry do not matter. */
+hla_status hla_linear_fwd(const hla_dims* d, const void* q, const void* k, const void* v,
+                          const void* g, void* out, int accumulate, float eps, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* Gated softmax anchor (non-causal, no mask, no positional term) -- the periodic
+ * gated-softmax layer that restores exact token interactions (SANA-Video 2.0
+ * abstract; lode.cx article, "The Core Innovation"). scale must be finite and
+ * > 0 (1/sqrt(D) is the usual choice). accumulate as in hla_linear_fwd. Needs
+ * no workspace. */
+hla_status hla_softmax_anchor_fwd(const hla_dims* d, const void* q, const void* k, const void* v,
+                                  const void* g, void* out, int accumulate, float scale,
+                                  void* stream);
+
+/* Hybrid stack: for l = 0 .. n_layers-1 in order, x += layer_l(q[l], k[l], v[l], g[l])
+ * where kinds[l] is HLA_LAYER_LINEAR or HLA_LAYER_SOFTMAX; SANA-Video 2.0 places a
+ * softmax anchor on every fourth layer (lode.cx article, "How It Works";
+ * ai-papers.net summary, section on hybrid linear attention). x has dtype
+ * d->out_dtype and is updated in place (an fp32 x keeps the residual stream
+ * exact to fp32 rounding). kinds, q, k, v, g are host arrays of n_layers
+ * entries; each q[l] ... g[l] is a device tensor like those of hla_linear_fwd.
+ * workspace as for hla_linear_fwd (needed only when some kind is linear; it
+ * may be NULL with workspace_bytes 0 otherwise). All layers are enqueued on
+ * `stream` in order. */
+hla_status hla_hybrid_stack_fwd(const hla_dims* d, int n_layers, const int32_t* kinds,
+                                const void* const* q, const void* const* k,
+                                const void* const* v, const void* const* g, void* x, float eps,
+                                float scale, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HLA_H */

@@ -1,0 +1,201 @@
+"""Python binding of libhla (hybrid linear-softmax attention on gfx950).
+
+A thin ctypes layer over the C ABI in include/hla.h, with the same names:
+``hla_linear_fwd``, ``hla_softmax_anchor_fwd``, ``hla_hybrid_stack_fwd``,
+``hla_linear_workspace_bytes``, ``hla_status_str``, ``hla_abi_version``. It only
+marshals arguments: torch tensors become device pointers and the current torch
+stream becomes the HIP stream; every step of the computation runs in the HIP
+kernels. The shared library must have been built (``python -m
+softmax_attention_amd.build``); importing this package without it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Sequence
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libhla.so")
+
+HLA_F32 = 0
+HLA_BF16 = 1
+HLA_LAYER_LINEAR = 0
+HLA_LAYER_SOFTMAX = 1
+STATUS = {
+    0: "HLA_OK", 1: "HLA_ERR_NULL_PTR", 2: "HLA_ERR_BAD_SHAPE", 3: "HLA_ERR_UNSUPPORTED",
+    4: "HLA_ERR_BAD_ARG", 5: "HLA_ERR_ALIGN", 6: "HLA_ERR_WORKSPACE", 7: "HLA_ERR_HIP",
+}
+EXPORTS = ("hla_abi_version", "hla_status_str", "hla_linear_workspace_bytes", "hla_linear_fwd",
+           "hla_softmax_anchor_fwd", "hla_hybrid_stack_fwd")
+
+
+class hla_dims(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("N", ctypes.c_int64),
+                ("D", ctypes.c_int64), ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32)]
+
+
+class HLAError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} returned {STATUS.get(status, status)}")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m softmax_attention_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    pd = ctypes.POINTER(hla_dims)
+    lib.hla_abi_version.restype = ctypes.c_int
+    lib.hla_abi_version.argtypes = []
+    lib.hla_status_str.restype = ctypes.c_char_p
+    lib.hla_status_str.argtypes = [ctypes.c_int]
+    lib.hla_linear_workspace_bytes.restype = ctypes.c_size_t
+    lib.hla_linear_workspace_bytes.argtypes = [pd]
+    lib.hla_linear_fwd.restype = ctypes.c_int
+    lib.hla_linear_fwd.argtypes = [pd, P, P, P, P, P, ctypes.c_int, ctypes.c_float, P,
+                                   ctypes.c_size_t, P]
+    lib.hla_softmax_anchor_fwd.restype = ctypes.c_int
+    lib.hla_softmax_anchor_fwd.argtypes = [pd, P, P, P, P, P, ctypes.c_int, ctypes.c_float, P]
+    lib.hla_hybrid_stack_fwd.restype = ctypes.c_int
+    lib.hla_hybrid_stack_fwd.argtypes = [pd, ctypes.c_int, ctypes.POINTER(ctypes.c_int32),
+                                         ctypes.POINTER(P), ctypes.POINTER(P), ctypes.POINTER(P),
+                                         ctypes.POINTER(P), P, ctypes.c_float, ctypes.c_float, P,
+                                         ctypes.c_size_t, P]
+    return lib
+
+
+lib = _load()
+
+
+def hla_abi_version() -> int:
+    return lib.hla_abi_version()
+
+
+def hla_status_str(status: int) -> str:
+    return lib.hla_status_str(status).decode()
+
+
+# ----------------------------------------------------------------------------
+# torch marshalling
+# ----------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return HLA_F32
+    if t.dtype == torch.bfloat16:
+        return HLA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def dims_of(q, out_dtype=None) -> hla_dims:
+    if q.dim() != 4:
+        raise ValueError(f"expected [B, H, N, D], got shape {tuple(q.shape)}")
+    B, H, N, D = (int(x) for x in q.shape)
+    ind = _dtype_code(q)
+    outd = ind if out_dtype is None else _dtype_code(out_dtype) if not isinstance(out_dtype, int) else out_dtype
+    return hla_dims(B, H, N, D, ind, outd)
+
+
+def _check(*ts):
+    ref = ts[0]
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous [B, H, N, D]")
+        if t.shape != ref.shape:
+            raise ValueError(f"shape mismatch {tuple(t.shape)} vs {tuple(ref.shape)}")
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+def _raise(fn: str, st: int):
+    if st != 0:
+        raise HLAError(fn, st)
+
+
+def hla_linear_workspace_bytes(dims: hla_dims) -> int:
+    return int(lib.hla_linear_workspace_bytes(ctypes.byref(dims)))
+
+
+def linear_workspace(q, out_dtype=None):
+    """A device workspace tensor sized for hla_linear_fwd / hla_hybrid_stack_fwd on q's shape."""
+    torch = _torch()
+    d = dims_of(q, out_dtype)
+    n = hla_linear_workspace_bytes(d)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
+
+
+def hla_linear_fwd(q, k, v, g, out=None, accumulate: bool = False, eps: float = 1e-6,
+                   workspace=None, stream=None):
+    """Gated linear attention O = sigma(G) * (phi(Q) S) / (phi(Q) z + eps); returns out."""
+    torch = _torch()
+    _check(q, k, v, g)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(q, out)
+    d = dims_of(q, out.dtype)
+    if workspace is None:
+        workspace = linear_workspace(q, out.dtype)
+    st = lib.hla_linear_fwd(ctypes.byref(d), q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(),
+                            out.data_ptr(), int(bool(accumulate)), float(eps), workspace.data_ptr(),
+                            workspace.numel() * workspace.element_size(), _stream(stream))
+    _raise("hla_linear_fwd", st)
+    return out
+
+
+def hla_softmax_anchor_fwd(q, k, v, g, out=None, accumulate: bool = False,
+                           scale: Optional[float] = None, stream=None):
+    """Gated softmax anchor O = sigma(G) * softmax(scale Q K^T) V; returns out."""
+    torch = _torch()
+    _check(q, k, v, g)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(q, out)
+    d = dims_of(q, out.dtype)
+    scale = 1.0 / math.sqrt(q.shape[-1]) if scale is None else float(scale)
+    st = lib.hla_softmax_anchor_fwd(ctypes.byref(d), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                    g.data_ptr(), out.data_ptr(), int(bool(accumulate)), scale,
+                                    _stream(stream))
+    _raise("hla_softmax_anchor_fwd", st)
+    return out
+
+
+def hla_hybrid_stack_fwd(x, layers: Sequence, kinds: Sequence[int], eps: float = 1e-6,
+                         scale: Optional[float] = None, workspace=None, stream=None):
+    """x += layer_l(q_l, k_l, v_l, g_l) for each layer in order (in place); returns x."""
+    n = len(layers)
+    if n != len(kinds):
+        raise ValueError("layers and kinds differ in length")
+    for (q, k, v, g) in layers:
+        _check(q, k, v, g)
+        _check(q, x)
+    q0 = layers[0][0]
+    d = dims_of(q0, x.dtype)
+    scale = 1.0 / math.sqrt(q0.shape[-1]) if scale is None else float(scale)
+    if workspace is None and any(kd == HLA_LAYER_LINEAR for kd in kinds):
+        workspace = linear_workspace(q0, x.dtype)
+    arr = ctypes.c_void_p * n
+    qs = arr(*[l[0].data_ptr() for l in layers])
+    ks = arr(*[l[1].data_ptr() for l in layers])
+    vs = arr(*[l[2].data_ptr() for l in layers])
+    gs = arr(*[l[3].data_ptr() for l in layers])
+    kd = (ctypes.c_int32 * n)(*[int(x_) for x_ in kinds])
+    wp = workspace.data_ptr() if workspace is not None else None
+    wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.hla_hybrid_stack_fwd(ctypes.byref(d), n, kd, qs, ks, vs, gs, x.data_ptr(), float(eps),
+                                  scale, wp, wb, _stream(stream))
+    _raise("hla_hybrid_stack_fwd", st)
+    return x

@@ -1,0 +1,201 @@
+// C ABI of the hybrid linear-softmax attention library (declared in include/hla.h).
+//
+// Every argument is validated on the host before any HIP call, so an invalid
+// call enqueues nothing and leaves the output untouched; the validation path
+// runs without a GPU. Valid calls enqueue kernels on the caller's stream and
+// return without synchronising.
+#include <math.h>
+#include <stdlib.h>
+
+#include "hla_internal.h"
+
+namespace hla {
+
+// Work-split overrides for tuning sweeps, read once from the environment
+// (HLA_LINEAR_CHUNKS, HLA_LINEAR_OUT_WGS); unset or 0 keeps the built-in choice.
+Tuning& tuning() {
+  static Tuning t = [] {
+    Tuning x;
+    if (const char* e = getenv("HLA_LINEAR_CHUNKS")) x.linear_chunks = atoi(e);
+    if (const char* e = getenv("HLA_LINEAR_OUT_WGS")) x.linear_out_wgs = atoi(e);
+    return x;
+  }();
+  return t;
+}
+
+namespace {
+
+constexpr int64_t kMaxIndex = 0x7fffffffLL;  // per-head offsets are 32-bit in places
+
+bool dtype_ok(int32_t x) { return x == HLA_F32 || x == HLA_BF16; }
+
+size_t elem_bytes(int32_t dt) { return dt == HLA_F32 ? 4 : 2; }
+
+// Shape and dtype checks shared by all entry points.
+hla_status check_dims(const hla_dims* d) {
+  if (!d) return HLA_ERR_NULL_PTR;
+  if (d->B < 0 || d->H < 0 || d->N < 0 || d->D <= 0) return HLA_ERR_BAD_SHAPE;
+  if (!dtype_ok(d->in_dtype) || !dtype_ok(d->out_dtype)) return HLA_ERR_UNSUPPORTED;
+  if (d->in_dtype == HLA_F32) {
+    if (d->out_dtype != HLA_F32) return HLA_ERR_UNSUPPORTED;
+    if (d->D != 32 && d->D != 64 && d->D != 128) return HLA_ERR_UNSUPPORTED;
+  } else {
+    if (d->D != 64 && d->D != 128) return HLA_ERR_UNSUPPORTED;
+  }
+  // every count must fit: B*H (grid), N*D (per-head offsets), B*H*N*D*4 bytes
+  if (d->B > kMaxIndex || d->H > kMaxIndex || d->N > kMaxIndex) return HLA_ERR_BAD_SHAPE;
+  const int64_t bh = d->B * d->H;  // < 2^62, no overflow
+  if (bh > 65535 * 1024LL) return HLA_ERR_BAD_SHAPE;
+  if (d->N * d->D > kMaxIndex) return HLA_ERR_BAD_SHAPE;
+  if (bh > 0 && d->N * d->D > INT64_MAX / 4 / bh) return HLA_ERR_BAD_SHAPE;
+  // anchor grid: B*H * ceil(N/128) workgroups in one dimension
+  if (bh * ((d->N + 127) / 128) > kMaxIndex) return HLA_ERR_BAD_SHAPE;
+  return HLA_OK;
+}
+
+bool empty(const hla_dims* d) { return d->B * d->H * d->N == 0; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+hla_status check_tensors(const void* q, const void* k, const void* v, const void* g,
+                         const void* out) {
+  if (!q || !k || !v || !g || !out) return HLA_ERR_NULL_PTR;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(out))
+    return HLA_ERR_ALIGN;
+  return HLA_OK;
+}
+
+hla_status from_hip(hipError_t e) { return e == hipSuccess ? HLA_OK : HLA_ERR_HIP; }
+
+}  // namespace
+
+LinearPlan linear_plan(const hla_dims& d) {
+  LinearPlan p;
+  const int64_t BH = d.B * d.H, N = d.N, D = d.D;
+  if (BH <= 0 || N <= 0) return p;
+  // state pass: aim at ~512 workgroups (two per CU) with chunks of >= 64 tokens
+  const int64_t max_c = (N + 63) / 64;
+  int64_t c = tuning().linear_chunks > 0 ? tuning().linear_chunks : (512 + BH - 1) / BH;
+  c = c < 1 ? 1 : (c > max_c ? max_c : c);
+  int64_t T = (N + c - 1) / c;
+  T = (T + 63) / 64 * 64;
+  c = (N + T - 1) / T;  // every chunk non-empty
+  p.C = int(c);
+  p.T = int(T);
+  // output pass: workgroups per head
+  int64_t P = tuning().linear_out_wgs > 0 ? tuning().linear_out_wgs : (512 + BH - 1) / BH;
+  const int64_t max_p = (N + 63) / 64;
+  P = P < 1 ? 1 : (P > max_p ? max_p : P);
+  p.P = int(P);
+  const size_t part = size_t(BH) * size_t(c) * size_t(D * D + D) * 4;
+  if (d.in_dtype == HLA_BF16)
+    p.state_bytes = size_t((D / 16 + 1) * (D / 32)) * 1024;  // MFMA operand fragments
+  else
+    p.state_bytes = size_t(D * D + D) * 4;                   // fp32 S and z
+  p.part_off = 0;
+  p.state_off = align_up(part, 256);
+  p.total = p.state_off + align_up(size_t(BH) * p.state_bytes, 256);
+  return p;
+}
+
+}  // namespace hla
+
+using namespace hla;
+
+extern "C" {
+
+int hla_abi_version(void) { return HLA_ABI_VERSION; }
+
+const char* hla_status_str(int s) {
+  switch (s) {
+    case HLA_OK: return "HLA_OK";
+    case HLA_ERR_NULL_PTR: return "HLA_ERR_NULL_PTR";
+    case HLA_ERR_BAD_SHAPE: return "HLA_ERR_BAD_SHAPE";
+    case HLA_ERR_UNSUPPORTED: return "HLA_ERR_UNSUPPORTED";
+    case HLA_ERR_BAD_ARG: return "HLA_ERR_BAD_ARG";
+    case HLA_ERR_ALIGN: return "HLA_ERR_ALIGN";
+    case HLA_ERR_WORKSPACE: return "HLA_ERR_WORKSPACE";
+    case HLA_ERR_HIP: return "HLA_ERR_HIP";
+    default: return "HLA_UNKNOWN";
+  }
+}
+
+size_t hla_linear_workspace_bytes(const hla_dims* d) {
+  if (check_dims(d) != HLA_OK || empty(d)) return 0;
+  return linear_plan(*d).total;
+}
+
+hla_status hla_linear_fwd(const hla_dims* d, const void* q, const void* k, const void* v,
+                          const void* g, void* out, int accumulate, float eps, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  hla_status st = check_dims(d);
+  if (st != HLA_OK) return st;
+  if (!isfinite(eps) || eps < 0.f || (accumulate != 0 && accumulate != 1)) return HLA_ERR_BAD_ARG;
+  if (empty(d)) return HLA_OK;
+  if ((st = check_tensors(q, k, v, g, out)) != HLA_OK) return st;
+  const LinearPlan plan = linear_plan(*d);
+  if (!workspace) return HLA_ERR_NULL_PTR;
+  if (!aligned16(workspace)) return HLA_ERR_ALIGN;
+  if (workspace_bytes < plan.total) return HLA_ERR_WORKSPACE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (d->in_dtype == HLA_BF16)
+    return from_hip(launch_linear_bf16(*d, q, k, v, g, out, accumulate, eps, workspace, plan, s));
+  return from_hip(launch_linear_f32(*d, q, k, v, g, out, accumulate, eps, workspace, plan, s));
+}
+
+hla_status hla_softmax_anchor_fwd(const hla_dims* d, const void* q, const void* k, const void* v,
+                                  const void* g, void* out, int accumulate, float scale,
+                                  void* stream) {
+  hla_status st = check_dims(d);
+  if (st != HLA_OK) return st;
+  if (!isfinite(scale) || scale <= 0.f || (accumulate != 0 && accumulate != 1))
+    return HLA_ERR_BAD_ARG;
+  if (empty(d)) return HLA_OK;
+  if ((st = check_tensors(q, k, v, g, out)) != HLA_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (d->in_dtype == HLA_BF16)
+    return from_hip(launch_anchor_bf16(*d, q, k, v, g, out, accumulate, scale, s));
+  return from_hip(launch_anchor_f32(*d, q, k, v, g, out, accumulate, scale, s));
+}
+
+hla_status hla_hybrid_stack_fwd(const hla_dims* d, int n_layers, const int32_t* kinds,
+                                const void* const* q, const void* const* k,
+                                const void* const* v, const void* const* g, void* x, float eps,
+                                float scale, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  hla_status st = check_dims(d);
+  if (st != HLA_OK) return st;
+  if (n_layers <= 0) return HLA_ERR_BAD_ARG;
+  if (!kinds || !q || !k || !v || !g) return HLA_ERR_NULL_PTR;
+  if (!isfinite(eps) || eps < 0.f || !isfinite(scale) || scale <= 0.f) return HLA_ERR_BAD_ARG;
+  bool any_linear = false;
+  for (int l = 0; l < n_layers; ++l) {
+    if (kinds[l] != HLA_LAYER_LINEAR && kinds[l] != HLA_LAYER_SOFTMAX) return HLA_ERR_BAD_ARG;
+    any_linear |= kinds[l] == HLA_LAYER_LINEAR;
+  }
+  if (empty(d)) return HLA_OK;
+  for (int l = 0; l < n_layers; ++l)
+    if ((st = check_tensors(q[l], k[l], v[l], g[l], x)) != HLA_OK) return st;
+  LinearPlan plan;
+  if (any_linear) {
+    plan = linear_plan(*d);
+    if (!workspace) return HLA_ERR_NULL_PTR;
+    if (!aligned16(workspace)) return HLA_ERR_ALIGN;
+    if (workspace_bytes < plan.total) return HLA_ERR_WORKSPACE;
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const bool bf = d->in_dtype == HLA_BF16;
+  for (int l = 0; l < n_layers; ++l) {
+    hipError_t e;
+    if (kinds[l] == HLA_LAYER_LINEAR)
+      e = bf ? launch_linear_bf16(*d, q[l], k[l], v[l], g[l], x, 1, eps, workspace, plan, s)
+             : launch_linear_f32(*d, q[l], k[l], v[l], g[l], x, 1, eps, workspace, plan, s);
+    else
+      e = bf ? launch_anchor_bf16(*d, q[l], k[l], v[l], g[l], x, 1, scale, s)
+             : launch_anchor_f32(*d, q[l], k[l], v[l], g[l], x, 1, scale, s);
+    if (e != hipSuccess) return HLA_ERR_HIP;
+  }
+  return HLA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// Host-side plumbing shared by the C-ABI entry points and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/hla.h"
+
+namespace hla {
+
+// Work split and workspace layout of the gated linear attention for one call.
+struct LinearPlan {
+  int C = 0;               // token chunks per (b, h) in the state pass
+  int T = 0;               // tokens per chunk (multiple of 64)
+  int P = 0;               // workgroups per (b, h) in the output pass
+  size_t part_off = 0;     // fp32 partial states [BH][C][D*D + D]
+  size_t state_off = 0;    // reduced state in the output pass's operand form
+  size_t state_bytes = 0;  // bytes per (b, h) of that form
+  size_t total = 0;        // workspace bytes
+};
+
+LinearPlan linear_plan(const hla_dims& d);
+
+// Work-split overrides (for sweeps); 0 keeps the built-in choice.
+struct Tuning {
+  int linear_chunks = 0;      // C override
+  int linear_out_wgs = 0;     // P override
+};
+Tuning& tuning();
+
+hipError_t launch_linear_bf16(const hla_dims& d, const void* q, const void* k, const void* v,
+                              const void* g, void* out, int accumulate, float eps, void* ws,
+                              const LinearPlan& plan, hipStream_t stream);
+hipError_t launch_linear_f32(const hla_dims& d, const void* q, const void* k, const void* v,
+                             const void* g, void* out, int accumulate, float eps, void* ws,
+                             const LinearPlan& plan, hipStream_t stream);
+hipError_t launch_anchor_bf16(const hla_dims& d, const void* q, const void* k, const void* v,
+                              const void* g, void* out, int accumulate, float scale,
+                              hipStream_t stream);
+hipError_t launch_anchor_f32(const hla_dims& d, const void* q, const void* k, const void* v,
+                             const void* g, void* out, int accumulate, float scale,
+                             hipStream_t stream);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace hla

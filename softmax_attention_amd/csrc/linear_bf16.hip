@@ -1,0 +1,356 @@
+// Gated linear attention, bf16 inputs, on gfx950 matrix cores.
+//
+// Three launches per call:
+//   1. state pass   per (token chunk, b, h): S_c = phi(K_c)^T V_c and
+//                   z_c = sum phi(K_c), with the contraction over tokens on
+//                   32x32x16 bf16 MFMA (fp32 accumulate); partials to workspace.
+//   2. reduce       per (b, h): S = sum_c S_c and z = sum_c z_c in a fixed chunk
+//                   order (deterministic, no float atomics), written straight into
+//                   the operand fragments the output pass feeds to the MFMA:
+//                   S^T rounded to bf16, z split into a bf16 hi + lo pair.
+//   3. output pass  per (b, h, token group): O = sigma(G) (.) (phi(Q) S) /
+//                   (phi(Q) . z + eps) with 16x16x32 bf16 MFMA, streaming Q and G
+//                   from HBM and writing O once.
+// The operator is the O(N) fixed-size-state token mixer of SANA-Video 2.0
+// (ai-papers.net summary, section on hybrid linear attention; SANA-Video 2.0
+// abstract on thelatestinai.com).
+#include "hla_device.h"
+#include "hla_internal.h"
+
+namespace hla {
+namespace {
+
+constexpr int kTile = 64;  // tokens per LDS tile in the state pass
+
+// ---------------------------------------------------------------------------
+// 1. state pass
+// ---------------------------------------------------------------------------
+// Wave w owns a (D/2 x D/2) quadrant of S: 32-row blocks [(w>>1)*RB, +RB) and
+// 32-column blocks [(w&1)*RB, +RB). MFMA operand A is phi(K)^T (rows = features,
+// k = tokens) and B is V (k = tokens, cols = features); both read 8 tokens of one
+// feature per lane out of a row-major LDS tile.
+template <int D>
+__global__ __launch_bounds__(256) void linear_state_bf16(const uint16_t* __restrict__ K,
+                                                         const uint16_t* __restrict__ V,
+                                                         float* __restrict__ part, int N, int T,
+                                                         int C) {
+  constexpr int CH = D / 8;                // 16-byte chunks per token row
+  constexpr int LOADS = kTile * CH / 256;  // 16-byte loads per thread per tensor per tile
+  constexpr int RS = D + 8;                // LDS row stride in elements (pads banks)
+  constexpr int RB = D / 64;               // 32-wide blocks per wave per side
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[kTile * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[kTile * RS];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = blockIdx.x, bh = blockIdx.y;
+  const int n0 = c * T;
+  const int n1 = min(N, n0 + T);
+  const size_t base = (size_t)bh * N * D;
+  const uint16_t* Kh = K + base;
+  const uint16_t* Vh = V + base;
+
+  u32x4 kr[LOADS], vr[LOADS];
+  float zacc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) zacc[e] = 0.f;
+  f32x16 acc[RB][RB];
+#pragma unroll
+  for (int x = 0; x < RB; ++x)
+#pragma unroll
+    for (int y = 0; y < RB; ++y) acc[x][y] = (f32x16){};
+
+  auto load_tile = [&](int t0) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int chunk = tid + 256 * i;
+      const int n = t0 + chunk / CH, col = (chunk % CH) * 8;
+      if (n < n1) {
+        kr[i] = ldg16(Kh + (size_t)n * D + col);
+        vr[i] = ldg16(Vh + (size_t)n * D + col);
+      } else {
+        kr[i] = (u32x4){0, 0, 0, 0};
+        vr[i] = (u32x4){0, 0, 0, 0};
+      }
+    }
+  };
+
+  const int r = lane & 31, h = lane >> 5;
+  const int ib0 = (wave >> 1) * RB, jb0 = (wave & 1) * RB;
+  const int ntiles = (n1 - n0 + kTile - 1) / kTile;
+
+  load_tile(n0);
+  for (int it = 0; it < ntiles; ++it) {
+    __syncthreads();  // every wave is done reading the previous tile
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int chunk = tid + 256 * i;
+      const int row = chunk / CH, col = (chunk % CH) * 8;
+      const u32x4 kk = relu_bf16x8(kr[i]);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        zacc[2 * p] += bf_lo(kk[p]);
+        zacc[2 * p + 1] += bf_hi(kk[p]);
+      }
+      *reinterpret_cast<u32x4*>(&Ks[row * RS + col]) = kk;
+      *reinterpret_cast<u32x4*>(&Vs[row * RS + col]) = vr[i];
+    }
+    __syncthreads();
+    if (it + 1 < ntiles) load_tile(n0 + (it + 1) * kTile);  // in flight during the MFMAs
+#pragma unroll
+    for (int s = 0; s < kTile / 16; ++s) {
+      const int tok = 16 * s + 8 * h;
+      u32x4 a[RB], b[RB];
+#pragma unroll
+      for (int x = 0; x < RB; ++x) {
+        const int fi = (ib0 + x) * 32 + r;
+        const int fj = (jb0 + x) * 32 + r;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          a[x][p] = uint32_t(Ks[(tok + 2 * p) * RS + fi]) |
+                    (uint32_t(Ks[(tok + 2 * p + 1) * RS + fi]) << 16);
+          b[x][p] = uint32_t(Vs[(tok + 2 * p) * RS + fj]) |
+                    (uint32_t(Vs[(tok + 2 * p + 1) * RS + fj]) << 16);
+        }
+      }
+#pragma unroll
+      for (int x = 0; x < RB; ++x)
+#pragma unroll
+        for (int y = 0; y < RB; ++y) acc[x][y] = mfma32x32x16(a[x], b[y], acc[x][y]);
+    }
+  }
+
+  // partial S: C-tile element (q*4 + e) of lane (col r, half h) is row q*8 + 4h + e
+  float* P = part + ((size_t)bh * C + c) * (size_t)(D * D + D);
+#pragma unroll
+  for (int x = 0; x < RB; ++x)
+#pragma unroll
+    for (int y = 0; y < RB; ++y)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = (ib0 + x) * 32 + q * 8 + 4 * h + e;
+          const int col = (jb0 + y) * 32 + r;
+          P[row * D + col] = acc[x][y][q * 4 + e];
+        }
+
+  // partial z: thread tid always loaded feature chunk (tid % CH); sum the
+  // 256/CH threads of each chunk in a fixed order
+  __syncthreads();
+  float* zred = reinterpret_cast<float*>(Ks);  // 8 KB, fits in the K tile
+#pragma unroll
+  for (int e = 0; e < 8; ++e) zred[tid * 8 + e] = zacc[e];
+  __syncthreads();
+  if (tid < D) {
+    const int cc = tid / 8, e = tid % 8;
+    float s = 0.f;
+    for (int m = 0; m < 256 / CH; ++m) s += zred[(cc + CH * m) * 8 + e];
+    P[D * D + tid] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 2. fixed-order reduce of the partial states into output-pass fragments
+// ---------------------------------------------------------------------------
+// Output pass MFMA (16x16x32): A rows i = lane & 15, k = 8*(lane>>4) + e.
+// Fragment (jb, t) of the numerator holds A[i][k] = S[32t + k][f(jb, i)] with
+// f(jb, i) = 32*(jb>>1) + 8*(i>>2) + 4*(jb&1) + (i&3), so that each output lane
+// ends with 8 consecutive features. Fragment (NJ, t) of the denominator holds
+// z_hi[32t + k] in rows 0..7 and z_lo[32t + k] in rows 8..15.
+template <int D>
+__global__ __launch_bounds__(256) void linear_reduce_bf16(const float* __restrict__ part,
+                                                          uint32_t* __restrict__ state, int C) {
+  constexpr int NT = D / 32, NJ = D / 16, NF = (NJ + 1) * NT;
+  const int jb = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  if (tid >= NT * 64) return;
+  const int t = tid >> 6, l = tid & 63, i = l & 15, g = l >> 4;
+  const size_t stride = (size_t)D * D + D;
+  const float* P = part + (size_t)bh * C * stride;
+  uint32_t w[4];
+  if (jb < NJ) {
+    const int f = 32 * (jb >> 1) + 8 * (i >> 2) + 4 * (jb & 1) + (i & 3);
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int row = 32 * t + 8 * g + e;
+      float s = 0.f;
+      for (int c = 0; c < C; ++c) s += P[c * stride + row * D + f];
+      v[e] = s;
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) w[p] = pack_bf16(v[2 * p], v[2 * p + 1]);
+  } else {
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int d = 32 * t + 8 * g + e;
+      float s = 0.f;
+      for (int c = 0; c < C; ++c) s += P[c * stride + D * D + d];
+      const float hi = bf16_to_f32(f32_to_bf16(s));
+      v[e] = (i < 8) ? hi : (s - hi);
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) w[p] = pack_bf16(v[2 * p], v[2 * p + 1]);
+  }
+  const int fi = (jb < NJ) ? jb * NT + t : NJ * NT + t;
+  uint32_t* dst = state + ((size_t)bh * NF + fi) * 256 + l * 4;
+  *reinterpret_cast<u32x4*>(dst) = (u32x4){w[0], w[1], w[2], w[3]};
+}
+
+// ---------------------------------------------------------------------------
+// 3. output pass
+// ---------------------------------------------------------------------------
+// Each wave takes 16 tokens at a time. Lane (n = lane & 15, g = lane >> 4) loads
+// Q and G of token n at features 32t + 8g .. +7 (t = 0 .. D/32-1), which is both
+// its B-operand slice for k-step t and, by the fragment row order above, the
+// feature slice of its output values -- so Q, G and O each move as 16-byte
+// accesses with no shuffles.
+template <int D, bool OUT_F32>
+__global__ __launch_bounds__(256, 2) void linear_out_bf16(const uint16_t* __restrict__ Q,
+                                                       const uint16_t* __restrict__ G,
+                                                       void* __restrict__ out,
+                                                       const uint32_t* __restrict__ state, int N,
+                                                       float eps, int accumulate) {
+  constexpr int NT = D / 32, NJ = D / 16, NF = (NJ + 1) * NT;
+  __shared__ u32x4 fr[NF * 64];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int bh = blockIdx.y;
+  {
+    const u32x4* src = reinterpret_cast<const u32x4*>(state + (size_t)bh * NF * 256);
+    for (int x = tid; x < NF * 64; x += 256) fr[x] = src[x];
+  }
+  __syncthreads();
+
+  const int n = lane & 15, g = lane >> 4;
+  const size_t base = (size_t)bh * N * D;
+  const uint16_t* Qh = Q + base;
+  const uint16_t* Gh = G + base;
+  const int stride = gridDim.x * 4;
+  int grp = blockIdx.x * 4 + wave;
+  if (grp * 16 >= N) return;
+
+  u32x4 qv[NT], gv[NT];
+  auto load = [&](int gi, u32x4* qd, u32x4* gd) {
+    const int tok = gi * 16 + n;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (tok < N) {
+        qd[t] = ldg16(Qh + (size_t)tok * D + 32 * t + 8 * g);
+        gd[t] = ldg16(Gh + (size_t)tok * D + 32 * t + 8 * g);
+      } else {
+        qd[t] = (u32x4){0, 0, 0, 0};
+        gd[t] = (u32x4){0, 0, 0, 0};
+      }
+    }
+  };
+  load(grp, qv, gv);
+
+  for (; grp * 16 < N; grp += stride) {
+    u32x4 qn[NT], gn[NT];
+    const bool more = (grp + stride) * 16 < N;
+    if (more) load(grp + stride, qn, gn);
+
+    // Re-read the fragments from LDS every group: an opaque (always zero)
+    // offset keeps the compiler from hoisting all of them into registers,
+    // which would cost the occupancy this streaming loop needs.
+    int fo = lane;
+    asm volatile("" : "+v"(fo));
+    f32x4 acc[NJ], accd = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const u32x4 b = relu_bf16x8(qv[t]);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[j] = mfma16x16x32(fr[(j * NT + t) * 64 + fo], b, acc[j]);
+      accd = mfma16x16x32(fr[(NJ * NT + t) * 64 + fo], b, accd);
+    }
+    const float den = accd[0] + swap_halves(accd[0]) + eps;
+    const float rden = 1.0f / den;
+
+    const int tok = grp * 16 + n;
+    if (tok < N) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          o[e] = acc[2 * t][e];
+          o[4 + e] = acc[2 * t + 1][e];
+        }
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          o[2 * p] = sigmoid(bf_lo(gv[t][p])) * (o[2 * p] * rden);
+          o[2 * p + 1] = sigmoid(bf_hi(gv[t][p])) * (o[2 * p + 1] * rden);
+        }
+        const size_t off = base + (size_t)tok * D + 32 * t + 8 * g;
+        if (OUT_F32) {
+          float* dst = reinterpret_cast<float*>(out) + off;
+          f32x4 lo = (f32x4){o[0], o[1], o[2], o[3]};
+          f32x4 hi = (f32x4){o[4], o[5], o[6], o[7]};
+          if (accumulate) {
+            lo += *reinterpret_cast<const f32x4*>(dst);
+            hi += *reinterpret_cast<const f32x4*>(dst + 4);
+          }
+          *reinterpret_cast<f32x4*>(dst) = lo;
+          *reinterpret_cast<f32x4*>(dst + 4) = hi;
+        } else {
+          uint16_t* dst = reinterpret_cast<uint16_t*>(out) + off;
+          if (accumulate) {
+            const u32x4 prev = ldg16(dst);
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+              o[2 * p] += bf_lo(prev[p]);
+              o[2 * p + 1] += bf_hi(prev[p]);
+            }
+          }
+          stg16(dst, (u32x4){pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]), pack_bf16(o[4], o[5]),
+                             pack_bf16(o[6], o[7])});
+        }
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        qv[t] = qn[t];
+        gv[t] = gn[t];
+      }
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_d(const hla_dims& d, const void* q, const void* k, const void* v, const void* g,
+                    void* out, int accumulate, float eps, void* ws, const LinearPlan& plan,
+                    hipStream_t stream) {
+  const int BH = int(d.B * d.H), N = int(d.N);
+  char* w = reinterpret_cast<char*>(ws);
+  float* part = reinterpret_cast<float*>(w + plan.part_off);
+  uint32_t* state = reinterpret_cast<uint32_t*>(w + plan.state_off);
+  hipLaunchKernelGGL(linear_state_bf16<D>, dim3(plan.C, BH), dim3(256), 0, stream,
+                     reinterpret_cast<const uint16_t*>(k), reinterpret_cast<const uint16_t*>(v),
+                     part, N, plan.T, plan.C);
+  hipLaunchKernelGGL(linear_reduce_bf16<D>, dim3(D / 16 + 1, BH), dim3(256), 0, stream, part,
+                     state, plan.C);
+  if (d.out_dtype == HLA_F32)
+    hipLaunchKernelGGL((linear_out_bf16<D, true>), dim3(plan.P, BH), dim3(256), 0, stream,
+                       reinterpret_cast<const uint16_t*>(q), reinterpret_cast<const uint16_t*>(g),
+                       out, state, N, eps, accumulate);
+  else
+    hipLaunchKernelGGL((linear_out_bf16<D, false>), dim3(plan.P, BH), dim3(256), 0, stream,
+                       reinterpret_cast<const uint16_t*>(q), reinterpret_cast<const uint16_t*>(g),
+                       out, state, N, eps, accumulate);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_linear_bf16(const hla_dims& d, const void* q, const void* k, const void* v,
+                              const void* g, void* out, int accumulate, float eps, void* ws,
+                              const LinearPlan& plan, hipStream_t stream) {
+  if (d.D == 128) return launch_d<128>(d, q, k, v, g, out, accumulate, eps, ws, plan, stream);
+  return launch_d<64>(d, q, k, v, g, out, accumulate, eps, ws, plan, stream);
+}
+
+}  // namespace hla

@@ -1,0 +1,162 @@
+// Gated linear attention, fp32 inputs, fp32 arithmetic throughout (vector ALU).
+//
+// Same three steps as the bf16 path -- per-chunk partial state, fixed-order
+// reduce, output pass -- but with plain fp32 FMAs so the result stays within
+// fp32 rounding of the exact operator. It serves the fp32 workloads, which are
+// small; the bf16 path is the fast one.
+#include "hla_device.h"
+#include "hla_internal.h"
+
+namespace hla {
+namespace {
+
+constexpr int kTileF = 32;  // tokens per LDS tile
+
+// partial S_c = phi(K_c)^T V_c and z_c; thread (ty, tx) owns an R x R block of S
+template <int D>
+__global__ __launch_bounds__(256) void linear_state_f32(const float* __restrict__ K,
+                                                        const float* __restrict__ V,
+                                                        float* __restrict__ part, int N, int T,
+                                                        int C) {
+  constexpr int R = D / 16;
+  __shared__ float Ks[kTileF][D];
+  __shared__ float Vs[kTileF][D];
+  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  const int c = blockIdx.x, bh = blockIdx.y;
+  const int n0 = c * T, n1 = min(N, n0 + T);
+  const size_t base = (size_t)bh * N * D;
+  float acc[R][R];
+  float z[R];
+#pragma unroll
+  for (int x = 0; x < R; ++x) {
+    z[x] = 0.f;
+#pragma unroll
+    for (int y = 0; y < R; ++y) acc[x][y] = 0.f;
+  }
+  for (int t0 = n0; t0 < n1; t0 += kTileF) {
+    __syncthreads();
+    for (int e = tid; e < kTileF * D; e += 256) {
+      const int row = e / D, col = e % D, n = t0 + row;
+      Ks[row][col] = n < n1 ? fmaxf(K[base + (size_t)n * D + col], 0.f) : 0.f;
+      Vs[row][col] = n < n1 ? V[base + (size_t)n * D + col] : 0.f;
+    }
+    __syncthreads();
+    for (int n = 0; n < kTileF; ++n) {
+      float a[R], b[R];
+#pragma unroll
+      for (int x = 0; x < R; ++x) {
+        a[x] = Ks[n][ty * R + x];
+        b[x] = Vs[n][tx * R + x];
+      }
+#pragma unroll
+      for (int x = 0; x < R; ++x) {
+        z[x] += a[x];
+#pragma unroll
+        for (int y = 0; y < R; ++y) acc[x][y] = fmaf(a[x], b[y], acc[x][y]);
+      }
+    }
+  }
+  float* P = part + ((size_t)bh * C + c) * (size_t)(D * D + D);
+#pragma unroll
+  for (int x = 0; x < R; ++x)
+#pragma unroll
+    for (int y = 0; y < R; ++y) P[(ty * R + x) * D + tx * R + y] = acc[x][y];
+  if (tx == 0) {
+#pragma unroll
+    for (int x = 0; x < R; ++x) P[D * D + ty * R + x] = z[x];
+  }
+}
+
+// S = sum_c S_c, z = sum_c z_c in chunk order; state is [BH][D*D + D] fp32
+template <int D>
+__global__ __launch_bounds__(256) void linear_reduce_f32(const float* __restrict__ part,
+                                                         float* __restrict__ state, int C) {
+  const size_t stride = (size_t)D * D + D;
+  const int e = blockIdx.x * 256 + threadIdx.x, bh = blockIdx.y;
+  if (e >= (int)stride) return;
+  const float* P = part + (size_t)bh * C * stride + e;
+  float s = 0.f;
+  for (int c = 0; c < C; ++c) s += P[c * stride];
+  state[(size_t)bh * stride + e] = s;
+}
+
+// O = sigma(G) (.) (phi(Q) S) / (phi(Q) . z + eps); thread (n, jg) owns D/8
+// outputs of token n; S streams through LDS 32 rows at a time
+template <int D>
+__global__ __launch_bounds__(256) void linear_out_f32(const float* __restrict__ Q,
+                                                      const float* __restrict__ G,
+                                                      float* __restrict__ out,
+                                                      const float* __restrict__ state, int N,
+                                                      float eps, int accumulate) {
+  constexpr int J = D / 8;
+  __shared__ float Qs[32][D];
+  __shared__ float Ss[32][D];
+  const int tid = threadIdx.x, n = tid >> 3, jg = tid & 7;
+  const int bh = blockIdx.y, t0 = blockIdx.x * 32;
+  const size_t base = (size_t)bh * N * D;
+  const float* S = state + (size_t)bh * (D * D + D);
+  const float* z = S + D * D;
+  for (int e = tid; e < 32 * D; e += 256) {
+    const int row = e / D, col = e % D, tok = t0 + row;
+    Qs[row][col] = tok < N ? fmaxf(Q[base + (size_t)tok * D + col], 0.f) : 0.f;
+  }
+  float acc[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) acc[j] = 0.f;
+  for (int i0 = 0; i0 < D; i0 += 32) {
+    __syncthreads();
+    for (int e = tid; e < 32 * D; e += 256) Ss[e / D][e % D] = S[(i0 + e / D) * D + e % D];
+    __syncthreads();
+    for (int ii = 0; ii < 32; ++ii) {
+      const float a = Qs[n][i0 + ii];
+#pragma unroll
+      for (int j = 0; j < J; ++j) acc[j] = fmaf(a, Ss[ii][jg * J + j], acc[j]);
+    }
+  }
+  float den = 0.f;
+  for (int i = 0; i < D; ++i) den = fmaf(Qs[n][i], z[i], den);
+  den += eps;
+  const int tok = t0 + n;
+  if (tok >= N) return;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const size_t off = base + (size_t)tok * D + jg * J + j;
+    const float gate = 1.0f / (1.0f + expf(-G[off]));
+    float o = gate * (acc[j] / den);
+    if (accumulate) o += out[off];
+    out[off] = o;
+  }
+}
+
+template <int D>
+hipError_t launch_d(const hla_dims& d, const void* q, const void* k, const void* v, const void* g,
+                    void* out, int accumulate, float eps, void* ws, const LinearPlan& plan,
+                    hipStream_t stream) {
+  const int BH = int(d.B * d.H), N = int(d.N);
+  char* w = reinterpret_cast<char*>(ws);
+  float* part = reinterpret_cast<float*>(w + plan.part_off);
+  float* state = reinterpret_cast<float*>(w + plan.state_off);
+  hipLaunchKernelGGL(linear_state_f32<D>, dim3(plan.C, BH), dim3(256), 0, stream,
+                     reinterpret_cast<const float*>(k), reinterpret_cast<const float*>(v), part, N,
+                     plan.T, plan.C);
+  hipLaunchKernelGGL(linear_reduce_f32<D>, dim3((D * D + D + 255) / 256, BH), dim3(256), 0,
+                     stream, part, state, plan.C);
+  hipLaunchKernelGGL(linear_out_f32<D>, dim3((N + 31) / 32, BH), dim3(256), 0, stream,
+                     reinterpret_cast<const float*>(q), reinterpret_cast<const float*>(g),
+                     reinterpret_cast<float*>(out), state, N, eps, accumulate);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_linear_f32(const hla_dims& d, const void* q, const void* k, const void* v,
+                             const void* g, void* out, int accumulate, float eps, void* ws,
+                             const LinearPlan& plan, hipStream_t stream) {
+  switch (d.D) {
+    case 32: return launch_d<32>(d, q, k, v, g, out, accumulate, eps, ws, plan, stream);
+    case 64: return launch_d<64>(d, q, k, v, g, out, accumulate, eps, ws, plan, stream);
+    default: return launch_d<128>(d, q, k, v, g, out, accumulate, eps, ws, plan, stream);
+  }
+}
+
+}  // namespace hla

@@ -1,0 +1,171 @@
+"""C-ABI checks that need no GPU: the library loads, exports what include/hla.h
+declares, and rejects every invalid argument on the host with its status code.
+
+Every call here carries at least one invalid argument (or an empty tensor), so
+validation returns before any HIP call: nothing is launched, which also keeps
+these tests safe to run on a machine that has a GPU.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import softmax_attention_amd as hla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hla.h")
+
+OK, NULLP, SHAPE, UNSUP, BADARG, ALIGN, WS, HIP = range(8)
+F32, BF16 = hla.HLA_F32, hla.HLA_BF16
+FAKE = 0x10000  # a 16-byte-aligned address that is never dereferenced
+ODD = 0x10008   # 8-byte aligned only
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(hla_[a-z0-9_]+)\s*\(", src)))
+
+
+def dims(B=2, H=3, N=100, D=128, i=BF16, o=BF16):
+    return hla.hla_dims(B, H, N, D, i, o)
+
+
+def lin(d, q=FAKE, k=FAKE, v=FAKE, g=FAKE, out=FAKE, acc=0, eps=1e-6, ws=FAKE, wsb=1 << 40):
+    return hla.lib.hla_linear_fwd(ctypes.byref(d) if d is not None else None, q, k, v, g, out, acc,
+                                  eps, ws, wsb, None)
+
+
+def sm(d, q=FAKE, k=FAKE, v=FAKE, g=FAKE, out=FAKE, acc=0, scale=0.1):
+    return hla.lib.hla_softmax_anchor_fwd(ctypes.byref(d) if d is not None else None, q, k, v, g,
+                                          out, acc, scale, None)
+
+
+def stack(d, n=2, kinds=(0, 1), ptrs=None, x=FAKE, eps=1e-6, scale=0.1, ws=FAKE, wsb=1 << 40):
+    arr = ctypes.c_void_p * max(n, 1)
+    p = ptrs if ptrs is not None else [FAKE] * max(n, 1)
+    q = arr(*p)
+    kd = (ctypes.c_int32 * max(len(kinds), 1))(*kinds) if kinds is not None else None
+    return hla.lib.hla_hybrid_stack_fwd(ctypes.byref(d) if d is not None else None, n, kd, q, q, q,
+                                        q, x, eps, scale, ws, wsb, None)
+
+
+def test_header_declares_the_abi():
+    fns = declared_functions()
+    assert fns == sorted(hla.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    for fn in declared_functions():
+        assert hasattr(hla.lib, fn), fn
+    out = subprocess.run(["nm", "-D", "--defined-only", hla.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    exported = set(re.findall(r" T (hla_[a-z0-9_]+)$", out, flags=re.M))
+    assert set(declared_functions()) <= exported
+
+
+def test_version_and_status_strings():
+    assert hla.hla_abi_version() == 1
+    for code, name in hla.STATUS.items():
+        assert hla.hla_status_str(code) == name
+    assert hla.hla_status_str(99) == "HLA_UNKNOWN"
+    assert hla.hla_status_str(-1) == "HLA_UNKNOWN"
+
+
+def test_workspace_bytes_pure_and_sized():
+    d = dims(2, 16, 19320, 128)
+    a = hla.hla_linear_workspace_bytes(d)
+    assert a == hla.hla_linear_workspace_bytes(dims(2, 16, 19320, 128)) and a > 0
+    # at least the partial states plus the reduced state of every head
+    assert a >= 2 * 16 * (128 * 128 + 128) * 4
+    assert a % 256 == 0
+    assert hla.hla_linear_workspace_bytes(dims(1, 2, 256, 32, F32, F32)) > 0
+    assert hla.hla_linear_workspace_bytes(dims(0, 2, 256, 32, F32, F32)) == 0      # empty
+    assert hla.hla_linear_workspace_bytes(dims(1, 2, 256, 48, F32, F32)) == 0      # unsupported D
+    assert hla.hla_linear_workspace_bytes(dims(1, 2, 256, 32, BF16, BF16)) == 0    # bf16 D=32 not built
+    assert hla.lib.hla_linear_workspace_bytes(None) == 0
+
+
+@pytest.mark.parametrize("call", ["lin", "sm"])
+def test_shape_and_dtype_errors(call):
+    f = lin if call == "lin" else sm
+    assert f(None) == NULLP
+    assert f(dims(B=-1)) == SHAPE
+    assert f(dims(N=-5)) == SHAPE
+    assert f(dims(D=0)) == SHAPE
+    assert f(dims(D=-128)) == SHAPE
+    assert f(dims(D=96)) == UNSUP
+    assert f(dims(D=32)) == UNSUP                  # bf16 path built for D in {64, 128}
+    assert f(dims(i=F32, o=BF16, D=32)) == UNSUP   # fp32 in -> bf16 out not built
+    assert f(dims(i=7)) == UNSUP
+    assert f(dims(o=2)) == UNSUP
+    assert f(dims(N=1 << 31)) == SHAPE             # N*D overflows 32-bit offsets
+    assert f(dims(B=1 << 40)) == SHAPE
+
+
+def test_linear_argument_errors():
+    d = dims()
+    for p in ("q", "k", "v", "g", "out"):
+        assert lin(d, **{p: None}) == NULLP, p
+        assert lin(d, **{p: ODD}) == ALIGN, p
+    assert lin(d, ws=None) == NULLP
+    assert lin(d, ws=ODD) == ALIGN
+    need = hla.hla_linear_workspace_bytes(d)
+    assert lin(d, wsb=need - 1) == WS
+    assert lin(d, wsb=0) == WS
+    for eps in (float("nan"), float("inf"), -1e-6):
+        assert lin(d, eps=eps) == BADARG
+    assert lin(d, acc=2) == BADARG
+    assert lin(d, acc=-1) == BADARG
+
+
+def test_softmax_argument_errors():
+    d = dims()
+    for p in ("q", "k", "v", "g", "out"):
+        assert sm(d, **{p: None}) == NULLP, p
+        assert sm(d, **{p: ODD}) == ALIGN, p
+    for s in (0.0, -0.1, float("nan"), float("inf")):
+        assert sm(d, scale=s) == BADARG
+    assert sm(d, acc=3) == BADARG
+
+
+def test_stack_argument_errors():
+    d = dims(o=F32)
+    assert stack(None) == NULLP
+    assert stack(d, n=0, kinds=(0,)) == BADARG
+    assert stack(d, n=-3, kinds=(0,)) == BADARG
+    assert stack(d, kinds=None) == NULLP
+    assert stack(d, kinds=(0, 2)) == BADARG
+    assert stack(d, kinds=(-1, 1)) == BADARG
+    assert stack(d, eps=float("nan")) == BADARG
+    assert stack(d, scale=0.0) == BADARG
+    assert stack(d, ptrs=[FAKE, None]) == NULLP
+    assert stack(d, ptrs=[FAKE, ODD]) == ALIGN
+    assert stack(d, x=None) == NULLP
+    assert stack(d, x=ODD) == ALIGN
+    assert stack(d, ws=None) == NULLP                           # has a linear layer
+    assert stack(d, wsb=hla.hla_linear_workspace_bytes(d) - 16) == WS
+    assert stack(dims(D=40, o=F32)) == UNSUP
+    assert stack(dims(N=-1, o=F32)) == SHAPE
+
+
+def test_empty_tensors_are_a_no_op():
+    # B*H*N == 0: valid, nothing to do, pointers may be NULL
+    for d in (dims(N=0), dims(B=0), dims(H=0, i=F32, o=F32, D=32)):
+        assert lin(d, q=None, k=None, v=None, g=None, out=None, ws=None, wsb=0) == OK
+        assert sm(d, q=None, k=None, v=None, g=None, out=None) == OK
+        assert stack(d, ptrs=[None, None], x=None, ws=None, wsb=0) == OK
+    # but the other arguments are still checked
+    assert lin(dims(N=0), eps=-1.0) == BADARG
+    assert sm(dims(N=0), scale=-1.0) == BADARG
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    t = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        hla.hla_linear_fwd(t, t, t, t)
+    with pytest.raises(ValueError):
+        hla.hla_softmax_anchor_fwd(t, t, t, t)

@@ -1,0 +1,259 @@
+"""GPU parity: the HIP path against the fp64 oracle, element by element (MI355X).
+
+Tolerances (metric: max |gpu - ref| / max |ref| per [b, h] slab, worst slab):
+  bf16 inputs, fp32 accumulation : 2e-2
+  fp32 path                      : 1e-4
+Any NaN/Inf fails. Small shapes span several tiles and ragged tails; the full
+workload sizes run in the same launch configuration the benchmark times, with
+the softmax anchor checked on sampled query rows that the oracle computes one
+by one (the linear layer is checked in full: its oracle is O(N)).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import softmax_attention_amd as hla
+from hla_inputs import WORKLOADS, BY_NAME, layer_inputs, residual_x0, custom
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.bfloat16: 2e-2, torch.float32: 1e-4}
+DEV = "cuda"
+
+
+def rel_err(got, ref):
+    return oracle.max_rel_error(got.float().cpu(), ref)
+
+
+def make(shape, seed, dtype):
+    return custom(shape, seed, dtype, n=4)
+
+
+def run_linear(q, k, v, g, eps=1e-6, out_dtype=None, accumulate=False, out=None):
+    qd, kd, vd, gd = (t.contiguous().to(DEV) for t in (q, k, v, g))
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=DEV)
+    hla.hla_linear_fwd(qd, kd, vd, gd, out=out, accumulate=accumulate, eps=eps)
+    torch.cuda.synchronize()
+    return out
+
+
+def run_softmax(q, k, v, g, scale=None, out_dtype=None, accumulate=False, out=None):
+    qd, kd, vd, gd = (t.contiguous().to(DEV) for t in (q, k, v, g))
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=DEV)
+    hla.hla_softmax_anchor_fwd(qd, kd, vd, gd, out=out, accumulate=accumulate, scale=scale)
+    torch.cuda.synchronize()
+    return out
+
+
+# ----------------------------------------------------------------------------
+# small shapes: tiles and ragged tails
+# ----------------------------------------------------------------------------
+
+TAIL_N = [1, 2, 3, 63, 64, 65, 127, 128, 129, 255, 257, 1000]
+
+
+@pytest.mark.parametrize("D", [128, 64])
+@pytest.mark.parametrize("N", TAIL_N)
+def test_linear_bf16_tails(N, D):
+    q, k, v, g = make((1, 2, N, D), 1000 + N + D, torch.bfloat16)
+    got = run_linear(q, k, v, g)
+    ref = oracle.gated_linear(q, k, v, g, 1e-6)
+    assert rel_err(got, ref) <= TOL[torch.bfloat16]
+
+
+@pytest.mark.parametrize("D", [128, 64])
+@pytest.mark.parametrize("N", TAIL_N)
+def test_softmax_bf16_tails(N, D):
+    q, k, v, g = make((1, 2, N, D), 2000 + N + D, torch.bfloat16)
+    got = run_softmax(q, k, v, g)
+    ref = oracle.gated_softmax(q, k, v, g, D ** -0.5)
+    assert rel_err(got, ref) <= TOL[torch.bfloat16]
+
+
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("N", [1, 33, 256, 1000])
+def test_fp32_paths(N, D):
+    q, k, v, g = make((2, 1, N, D), 3000 + N + D, torch.float32)
+    lin = run_linear(q, k, v, g)
+    assert rel_err(lin, oracle.gated_linear(q, k, v, g, 1e-6)) <= TOL[torch.float32]
+    sm = run_softmax(q, k, v, g)
+    assert rel_err(sm, oracle.gated_softmax(q, k, v, g, D ** -0.5)) <= TOL[torch.float32]
+
+
+def test_tiny_workload_fp32():
+    w = BY_NAME["tiny_f32"]
+    q, k, v, g = layer_inputs(w, 0)
+    assert rel_err(run_linear(q, k, v, g, w.eps), oracle.gated_linear(q, k, v, g, w.eps)) <= 1e-4
+    assert rel_err(run_softmax(q, k, v, g, w.scale), oracle.gated_softmax(q, k, v, g, w.scale)) <= 1e-4
+
+
+@pytest.mark.parametrize("op", ["linear", "softmax"])
+def test_bf16_accumulate_into_fp32_and_bf16(op):
+    N, D = 300, 128
+    q, k, v, g = make((1, 3, N, D), 4000, torch.bfloat16)
+    x0 = custom((1, 3, N, D), 4100, torch.float32, n=1)[0]
+    ref = (oracle.gated_linear(q, k, v, g, 1e-6) if op == "linear"
+           else oracle.gated_softmax(q, k, v, g, D ** -0.5))
+    run = run_linear if op == "linear" else run_softmax
+    x = x0.to(DEV)
+    run(q, k, v, g, accumulate=True, out=x)
+    # the residual update is checked on delta = x - x0 (x0 is far larger than O)
+    assert rel_err(x.cpu() - x0, ref) <= 2e-2
+    xb = x0.to(torch.bfloat16)
+    y = xb.to(DEV)
+    run(q, k, v, g, accumulate=True, out=y)
+    assert rel_err(y.float(), oracle.as_f64(xb) + ref) <= 2e-2
+
+
+# ----------------------------------------------------------------------------
+# special values and invariants
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("op", ["linear", "softmax"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_gate_extremes(op, dtype):
+    N, D = 200, 64
+    q, k, v, g = make((1, 2, N, D), 5000, dtype)
+    run = run_linear if op == "linear" else run_softmax
+    closed = run(q, k, v, torch.full_like(g, -float("inf")))
+    assert torch.all(closed == 0)
+    assert torch.all(run(q, k, v, torch.full_like(g, -1e4)) == 0)
+    full = run(q, k, v, torch.full_like(g, float("inf")))
+    half = run(q, k, v, torch.zeros_like(g))
+    assert torch.equal(half.float() * 2, full.float())
+
+
+def test_linear_zero_feature_rows_give_zero():
+    N, D = 130, 128
+    q, k, v, g = make((1, 2, N, D), 5100, torch.bfloat16)
+    q[:, :, ::7, :] = -q[:, :, ::7, :].abs()   # phi(Q_n) = 0 on every 7th token
+    got = run_linear(q, k, v, g)
+    assert torch.all(got[:, :, ::7, :] == 0)
+    assert rel_err(got, oracle.gated_linear(q, k, v, g, 1e-6)) <= 2e-2
+
+
+def test_linear_all_negative_keys():
+    # phi(K) = 0: S = 0, z = 0, every output is 0 / eps = 0
+    N, D = 100, 128
+    q, k, v, g = make((1, 1, N, D), 5200, torch.bfloat16)
+    got = run_linear(q, -k.abs(), v, g)
+    assert torch.all(got == 0)
+
+
+def test_softmax_constant_v_and_single_key():
+    N, D = 333, 128
+    q, k, v, g = make((1, 2, N, D), 5300, torch.bfloat16)
+    c = v[:, :, :1, :].expand(-1, -1, N, -1).contiguous()
+    got = run_softmax(q, k, c, g)
+    ref = oracle.sigmoid(oracle.as_f64(g)) * oracle.as_f64(c)
+    assert rel_err(got, ref) <= 2e-2
+    one = run_softmax(q[:, :, :1], k[:, :, :1], v[:, :, :1], g[:, :, :1])
+    ref1 = oracle.sigmoid(oracle.as_f64(g[:, :, :1])) * oracle.as_f64(v[:, :, :1])
+    assert rel_err(one, ref1) <= 1e-2
+
+
+def test_softmax_peaky_logits():
+    # Q scaled x4: sharply peaked rows exercise the running-max updates
+    N, D = 700, 128
+    q, k, v, g = make((1, 2, N, D), 5400, torch.float32)
+    q = (q * 4).to(torch.bfloat16)
+    k, v, g = (t.to(torch.bfloat16) for t in (k, v, g))
+    got = run_softmax(q, k, v, g)
+    assert rel_err(got, oracle.gated_softmax(q, k, v, g, D ** -0.5)) <= 2e-2
+
+
+@pytest.mark.parametrize("op", ["linear", "softmax"])
+def test_deterministic_and_in_bounds(op):
+    N, D = 517, 128
+    q, k, v, g = (t.to(DEV) for t in make((2, 2, N, D), 5500, torch.bfloat16))
+    n = q.numel()
+    guard = 4096
+    outs = []
+    for _ in range(2):
+        buf = torch.full((n + 2 * guard,), 7.0, dtype=torch.bfloat16, device=DEV)
+        out = buf[guard:guard + n].view(q.shape)
+        if op == "linear":
+            hla.hla_linear_fwd(q, k, v, g, out=out)
+        else:
+            hla.hla_softmax_anchor_fwd(q, k, v, g, out=out)
+        torch.cuda.synchronize()
+        assert torch.all(buf[:guard] == 7.0) and torch.all(buf[guard + n:] == 7.0)
+        outs.append(out.clone())
+    assert torch.equal(outs[0], outs[1])
+
+
+def test_empty_sequence_is_a_no_op():
+    q = torch.empty((1, 2, 0, 128), dtype=torch.bfloat16, device=DEV)
+    hla.hla_linear_fwd(q, q, q, q, out=torch.empty_like(q))
+    hla.hla_softmax_anchor_fwd(q, q, q, q, out=torch.empty_like(q))
+    torch.cuda.synchronize()
+
+
+# ----------------------------------------------------------------------------
+# full workload sizes, in the benchmark's launch configuration
+# ----------------------------------------------------------------------------
+
+def sample_rows(N, count=40, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(N, size=min(N, count), replace=False).tolist())
+    rows |= {0, N - 1, N - 2, (N // 128) * 128, max(0, (N // 128) * 128 - 1)}
+    return np.array(sorted(r for r in rows if 0 <= r < N))
+
+
+@pytest.mark.parametrize("name", ["480p_81f", "720p_81f", "long_720p_193f"])
+def test_full_workload(name):
+    w = BY_NAME[name]
+    q, k, v, g = layer_inputs(w, 0)
+    print(f"[{name}] B={w.B} H={w.H} N={w.N} D={w.D}", flush=True)
+    lin = run_linear(q, k, v, g, w.eps)
+    ref = oracle.gated_linear(q, k, v, g, w.eps)
+    e_lin = rel_err(lin, ref)
+    del ref
+    rows = sample_rows(w.N, seed=w.index)
+    sm = run_softmax(q, k, v, g, w.scale)
+    ref_s = oracle.gated_softmax(q, k, v, g, w.scale, rows=rows)
+    e_sm = rel_err(sm[..., rows, :], ref_s)
+    print(f"[{name}] linear err {e_lin:.3e}  softmax err {e_sm:.3e} on {len(rows)} rows", flush=True)
+    assert e_lin <= 2e-2
+    assert e_sm <= 2e-2
+
+
+def test_hybrid_stack_small_full():
+    # an 8-layer 3:1 stack at a size the oracle finishes quickly, checked in full
+    B, H, N, D = 1, 4, 777, 128
+    kinds = oracle.hybrid_kinds(8)
+    layers = [make((B, H, N, D), 6000 + 10 * l, torch.bfloat16) for l in range(8)]
+    x0 = custom((B, H, N, D), 6100, torch.float32, n=1)[0]
+    x = x0.to(DEV)
+    hla.hla_hybrid_stack_fwd(x, [tuple(t.to(DEV) for t in L) for L in layers], kinds)
+    torch.cuda.synchronize()
+    ref = oracle.hybrid_stack(x0, layers, kinds, 1e-6, D ** -0.5)
+    assert rel_err(x.cpu() - x0, ref - oracle.as_f64(x0)) <= 2e-2
+
+
+def test_hybrid_stack_workload_sampled():
+    # the 8-layer 720p x 121-frame stack; delta = x8 - x0 on sampled rows
+    w = BY_NAME["stack_720p_121f"]
+    kinds = list(w.kinds)
+    layers_cpu = [layer_inputs(w, l) for l in range(8)]
+    x0 = residual_x0(w)
+    x = x0.to(DEV)
+    layers = [tuple(t.to(DEV) for t in L) for L in layers_cpu]
+    hla.hla_hybrid_stack_fwd(x, layers, kinds, eps=w.eps, scale=w.scale)
+    torch.cuda.synchronize()
+    rows = sample_rows(w.N, seed=4)
+    delta = (x.cpu() - x0)[..., rows, :]
+    ref = np.zeros(delta.shape)
+    for kind, (q, k, v, g) in zip(kinds, layers_cpu):
+        if kind == oracle.LINEAR:
+            ref += oracle.gated_linear(q, k, v, g, w.eps)[..., rows, :]
+        else:
+            ref += oracle.gated_softmax(q, k, v, g, w.scale, rows=rows)
+    e = rel_err(delta, ref)
+    print(f"[stack] delta err {e:.3e}", flush=True)
+    assert e <= 2e-2

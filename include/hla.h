@@ -32,6 +32,8 @@
  * nothing is enqueued and the output is untouched. On success the work is
  * enqueued on `stream` (a hipStream_t; NULL means the null stream) and the call
  * returns without synchronising; device faults surface at the caller's next sync.
+ * Before launching, a call clears the calling thread's pending HIP error state
+ * (hipGetLastError), so that HLA_ERR_HIP reports only errors of its own launches.
  * A tensor with B*H*N == 0 is empty: after the checks the call returns HLA_OK and
  * enqueues nothing (pointers may then be NULL). Calls are reentrant; calls that
  * share a workspace must be ordered on one stream. out/x must not overlap any

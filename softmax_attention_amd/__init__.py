@@ -41,10 +41,29 @@ class HLAError(RuntimeError):
         self.status = status
 
 
+def hip_runtimes_loaded() -> list:
+    """Paths of the HIP runtime libraries mapped into this process."""
+    try:
+        with open("/proc/self/maps") as f:
+            maps = f.read()
+    except OSError:
+        return []
+    return sorted({line.split()[-1] for line in maps.splitlines()
+                   if "libamdhip64" in line and "/" in line})
+
+
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with `python -m softmax_attention_amd.build`")
+    # torch ships its own HIP runtime. Load it first so that libhla binds to that
+    # same runtime (same soname) instead of pulling in a second copy from
+    # /opt/rocm: device memory and streams come from torch, and two runtimes in
+    # one process cannot share them.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
+    runtimes = hip_runtimes_loaded()
+    if len(runtimes) > 1:
+        raise ImportError(f"more than one HIP runtime is loaded: {runtimes}")
     P = ctypes.c_void_p
     pd = ctypes.POINTER(hla_dims)
     lib.hla_abi_version.restype = ctypes.c_int
@@ -86,21 +105,24 @@ def _torch():
     return torch
 
 
-def _dtype_code(t) -> int:
+def _dtype_code(dt) -> int:
+    """hla_dtype of a torch dtype (or of a tensor's dtype)."""
     torch = _torch()
-    if t.dtype == torch.float32:
+    dt = getattr(dt, "dtype", dt)
+    if dt == torch.float32:
         return HLA_F32
-    if t.dtype == torch.bfloat16:
+    if dt == torch.bfloat16:
         return HLA_BF16
-    raise TypeError(f"unsupported dtype {t.dtype}")
+    raise TypeError(f"unsupported dtype {dt}")
 
 
 def dims_of(q, out_dtype=None) -> hla_dims:
+    """hla_dims of a [B, H, N, D] tensor; out_dtype defaults to q's dtype."""
     if q.dim() != 4:
         raise ValueError(f"expected [B, H, N, D], got shape {tuple(q.shape)}")
     B, H, N, D = (int(x) for x in q.shape)
     ind = _dtype_code(q)
-    outd = ind if out_dtype is None else _dtype_code(out_dtype) if not isinstance(out_dtype, int) else out_dtype
+    outd = ind if out_dtype is None else _dtype_code(out_dtype)
     return hla_dims(B, H, N, D, ind, outd)
 
 
@@ -123,6 +145,10 @@ def _stream(stream) -> int:
 
 def _raise(fn: str, st: int):
     if st != 0:
+        if st == 7:
+            # some launches may already be queued: let them finish before the
+            # caller's tensors can be freed
+            _torch().cuda.synchronize()
         raise HLAError(fn, st)
 
 

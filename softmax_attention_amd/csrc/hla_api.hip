@@ -67,6 +67,11 @@ hla_status check_tensors(const void* q, const void* k, const void* v, const void
 
 hla_status from_hip(hipError_t e) { return e == hipSuccess ? HLA_OK : HLA_ERR_HIP; }
 
+// hipGetLastError() also reports errors left pending by the caller's earlier
+// runtime calls (a failed pointer query, for instance). Clear that state right
+// before launching, so the check after the launches sees only this call's.
+void clear_pending_error() { (void)hipGetLastError(); }
+
 }  // namespace
 
 LinearPlan linear_plan(const hla_dims& d) {
@@ -138,6 +143,7 @@ hla_status hla_linear_fwd(const hla_dims* d, const void* q, const void* k, const
   if (!aligned16(workspace)) return HLA_ERR_ALIGN;
   if (workspace_bytes < plan.total) return HLA_ERR_WORKSPACE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  clear_pending_error();
   if (d->in_dtype == HLA_BF16)
     return from_hip(launch_linear_bf16(*d, q, k, v, g, out, accumulate, eps, workspace, plan, s));
   return from_hip(launch_linear_f32(*d, q, k, v, g, out, accumulate, eps, workspace, plan, s));
@@ -153,6 +159,7 @@ hla_status hla_softmax_anchor_fwd(const hla_dims* d, const void* q, const void* 
   if (empty(d)) return HLA_OK;
   if ((st = check_tensors(q, k, v, g, out)) != HLA_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  clear_pending_error();
   if (d->in_dtype == HLA_BF16)
     return from_hip(launch_anchor_bf16(*d, q, k, v, g, out, accumulate, scale, s));
   return from_hip(launch_anchor_f32(*d, q, k, v, g, out, accumulate, scale, s));
@@ -185,6 +192,7 @@ hla_status hla_hybrid_stack_fwd(const hla_dims* d, int n_layers, const int32_t* 
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool bf = d->in_dtype == HLA_BF16;
+  clear_pending_error();
   for (int l = 0; l < n_layers; ++l) {
     hipError_t e;
     if (kinds[l] == HLA_LAYER_LINEAR)

@@ -169,3 +169,25 @@ def test_binding_rejects_cpu_tensors():
         hla.hla_linear_fwd(t, t, t, t)
     with pytest.raises(ValueError):
         hla.hla_softmax_anchor_fwd(t, t, t, t)
+
+
+def test_binding_dims():
+    import torch
+    t = torch.zeros(2, 3, 5, 64, dtype=torch.bfloat16)
+    d = hla.dims_of(t, torch.float32)
+    assert (d.B, d.H, d.N, d.D, d.in_dtype, d.out_dtype) == (2, 3, 5, 64, BF16, F32)
+    d = hla.dims_of(t)
+    assert d.out_dtype == BF16
+    assert hla.dims_of(t.float(), t.float()).in_dtype == F32
+    with pytest.raises(TypeError):
+        hla.dims_of(t.half())
+
+
+def test_one_hip_runtime_whatever_the_import_order():
+    # libhla must bind to torch's HIP runtime even when imported before torch
+    import sys
+    code = ("import softmax_attention_amd as h, torch; "
+            "r = h.hip_runtimes_loaded(); print(len(r)); assert len(r) == 1, r")
+    res = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+    assert res.stdout.strip().endswith("1")

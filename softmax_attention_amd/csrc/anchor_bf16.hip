@@ -17,10 +17,14 @@
 //                    result exact up to rounding.
 //   O^T += V^T P^T   P^T stays in registers (the MFMA result layout is reused as
 //                    the next B operand by permuting the key order inside each
-//                    k-step); V is stored transposed in LDS so each lane reads
-//                    its 8 keys as two 8-byte loads.
+//                    k-step); V stays row-major in LDS and the V^T operand comes
+//                    from two LDS transpose reads per MFMA.
+// K and V tiles arrive through buffer loads, which return zeros past the end of
+// the head, so the last partial tile needs no predicated loads.
 // The epilogue divides by the row sum, applies the sigmoid gate and stores O
 // (bf16) or adds it into an fp32 residual stream.
+#include <type_traits>
+
 #include "hla_device.h"
 #include "hla_internal.h"
 
@@ -31,6 +35,26 @@ constexpr int kBR = 128;  // query rows per workgroup
 constexpr int kBC = 64;   // keys per LDS tile
 constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
 
+// LDS tiles are row-major (one key per row) with XOR swizzles of whole chunks
+// instead of padding:
+//   K: 16-byte chunk c of row k sits at chunk c ^ (k & 15) (c ^ (k & 7) for D=64),
+//      so the 32 rows one S^T operand read touches spread over all banks;
+//   V: 8-byte chunk c of row k sits at chunk c ^ kVx[k & 3], which keeps the
+//      transposed (ds_read_b64_tr_b16) operand reads of 16 lanes on 16 distinct
+//      bank pairs.
+template <int D>
+struct AnchorSwz;
+template <>
+struct AnchorSwz<128> {
+  static constexpr int kmask = 15;
+  __device__ static int vx8(int k) { return (0x18120a00 >> (8 * (k & 3))) & 0xff; }  // 0,10,18,24
+};
+template <>
+struct AnchorSwz<64> {
+  static constexpr int kmask = 7;
+  __device__ static int vx8(int k) { return (0x08020a00 >> (8 * (k & 3))) & 0xff; }  // 0,10,2,8
+};
+
 template <int D, bool OUT_F32>
 __global__ __launch_bounds__(256, 2) void anchor_bf16(const uint16_t* __restrict__ Q,
                                                       const uint16_t* __restrict__ K,
@@ -38,14 +62,14 @@ __global__ __launch_bounds__(256, 2) void anchor_bf16(const uint16_t* __restrict
                                                       const uint16_t* __restrict__ G,
                                                       void* __restrict__ out, int N, int nqb,
                                                       int total, float c, int accumulate) {
-  constexpr int KS = D + 8;        // K tile row stride (elements)
-  constexpr int VS = kBC + 4;      // V^T tile row stride (elements)
-  constexpr int NK = D / 16;       // k-steps of S^T
-  constexpr int ND = D / 32;       // 32-row blocks of O^T
-  constexpr int CH = D / 8;        // 16-byte chunks per row
-  constexpr int KLOADS = kBC * CH / 256;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kBC * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VS];
+  constexpr int NK = D / 16;              // k-steps of S^T
+  constexpr int ND = D / 32;              // 32-row blocks of O^T
+  constexpr int CH = D / 8;               // 16-byte chunks per row
+  constexpr int LOADS = kBC * CH / 256;   // 16-byte loads per thread per tensor per tile
+  constexpr uint32_t kTileBytes = kBC * D * 2;
+  using Swz = AnchorSwz<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kBC * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kBC * D];
 
   // Workgroups are dispatched round-robin over the 8 XCDs; renumber them so
   // each XCD runs a contiguous range of (b, h, query block) and the query
@@ -57,76 +81,84 @@ __global__ __launch_bounds__(256, 2) void anchor_bf16(const uint16_t* __restrict
       xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
   const int bh = logical / nqb, qb = logical - bh * nqb;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave index, made visibly wave-uniform (it selects the M0 LDS base of the
+  // direct-to-LDS loads, which must be a scalar)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 31, h = lane >> 5;
   const size_t base = (size_t)bh * N * D;
-  const uint16_t* Qh = Q + base;
-  const uint16_t* Kh = K + base;
-  const uint16_t* Vh = V + base;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
   const int qrow = qb * kBR + wave * 32 + r;
 
   u32x4 qf[NK];
+  {
+    const rsrc_t Qr = make_rsrc(Q + base, head_bytes);
+    const uint32_t qoff = qrow < N ? (uint32_t)qrow * D * 2 : head_bytes;  // past N reads 0
 #pragma unroll
-  for (int t = 0; t < NK; ++t)
-    qf[t] = qrow < N ? ldg16(Qh + (size_t)qrow * D + 16 * t + 8 * h) : (u32x4){0, 0, 0, 0};
+    for (int t = 0; t < NK; ++t) qf[t] = buf_load16(Qr, qoff + (16 * t + 8 * h) * 2);
+  }
 
-  // tile loaders: K row-major, V as 4 keys x 8 features per thread
-  const int kq = tid & 15, dc = tid >> 4;
-  const bool vload = dc < CH;
-  u32x4 kr[KLOADS], vr[4];
-  auto load_tile = [&](int j) {
-    const int k0 = j * kBC;
+  // Tiles go global -> LDS directly (buffer_load ... lds): instruction i of
+  // wave w fills the 1 KB LDS block bw = LOADS*w + i, i.e. rows 4bw..4bw+3 with
+  // lane l at row 4bw + l/16, physical 16-byte chunk l%16. Each lane fetches
+  // the logical chunk that the swizzle puts there.
+  constexpr int ROWS_PER_BLK = 1024 / (D * 2);   // 4 rows of 256 B (8 for D=64)
+  uint32_t goff_k[LOADS], goff_v[LOADS];
 #pragma unroll
-    for (int i = 0; i < KLOADS; ++i) {
-      const int chunk = tid + 256 * i;
-      const int key = k0 + chunk / CH, col = (chunk % CH) * 8;
-      kr[i] = key < N ? ldg16(Kh + (size_t)key * D + col) : (u32x4){0, 0, 0, 0};
-    }
-    if (vload) {
+  for (int i = 0; i < LOADS; ++i) {
+    const int blk = LOADS * wave + i;
+    const int row = blk * ROWS_PER_BLK + lane / CH, pc = lane % CH;
+    const int ck = pc ^ (row & Swz::kmask);
+    const int cv = (2 * pc ^ Swz::vx8(row)) / 2;
+    goff_k[i] = (row * D + ck * 8) * 2;
+    goff_v[i] = (row * D + cv * 8) * 2;
+  }
+  // issue tile j into LDS buffer buf (completion: wait_all_memory + barrier)
+  auto load_tile = [&](int j, int buf) {
+    const uint32_t done = (uint32_t)j * kTileBytes;
+    const uint32_t left = done < head_bytes ? head_bytes - done : 0u;
+    const rsrc_t kr = make_rsrc_uniform(K + base + (size_t)j * kBC * D, left);
+    const rsrc_t vr = make_rsrc_uniform(V + base + (size_t)j * kBC * D, left);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = k0 + 4 * kq + i;
-        vr[i] = key < N ? ldg16(Vh + (size_t)key * D + 8 * dc) : (u32x4){0, 0, 0, 0};
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KLOADS; ++i) {
-      const int chunk = tid + 256 * i;
-      const int row = chunk / CH, col = (chunk % CH) * 8;
-      *reinterpret_cast<u32x4*>(&Ks[buf][row * KS + col]) = kr[i];
-    }
-    if (vload) {
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const uint32_t e0 = (vr[0][p] & 0xffffu) | (vr[1][p] << 16);
-        const uint32_t e1 = (vr[2][p] & 0xffffu) | (vr[3][p] << 16);
-        const uint32_t o0 = (vr[0][p] >> 16) | (vr[1][p] & 0xffff0000u);
-        const uint32_t o1 = (vr[2][p] >> 16) | (vr[3][p] & 0xffff0000u);
-        *reinterpret_cast<u32x2*>(&Vt[buf][(8 * dc + 2 * p) * VS + 4 * kq]) = (u32x2){e0, e1};
-        *reinterpret_cast<u32x2*>(&Vt[buf][(8 * dc + 2 * p + 1) * VS + 4 * kq]) = (u32x2){o0, o1};
-      }
+    for (int i = 0; i < LOADS; ++i) {
+      const int blk = LOADS * wave + i;
+      buf_load16_lds(kr, goff_k[i], &Ks[buf][blk * 512]);
+      buf_load16_lds(vr, goff_v[i], &Vs[buf][blk * 512]);
     }
   };
+
+  // S^T operand A (key rows): lane reads row kb*32 + r, chunk 2t + h (swizzled)
+  int koff[NK];
+#pragma unroll
+  for (int t = 0; t < NK; ++t) koff[t] = r * D + (((2 * t + h) ^ (r & Swz::kmask)) * 8);
+  // O^T operand A (V^T) through transposed reads: source lane (e = (lane>>2)&3,
+  // q = lane&3) of each 16-lane group points at key 4h + e (+16 ks, +8 for the
+  // upper four k-slots) and at the 4 features of output rows R = 16 g + 4 q..+3,
+  // where MFMA row R maps to feature 16((R>>2)&1) + 4(R>>3) + (R&3) of block b.
+  const int ve = (lane >> 2) & 3, vq = lane & 3, vg = (lane >> 4) & 1;
+  const int vkey = 4 * h + ve;
+  int voff[ND];
+#pragma unroll
+  for (int b = 0; b < ND; ++b) {
+    const int chunk8 = b * 8 + 4 * (vq & 1) + (vq >> 1) + 2 * vg;
+    voff[b] = vkey * D + ((chunk8 ^ Swz::vx8(vkey)) * 4);
+  }
 
   f32x16 acc[ND];
 #pragma unroll
   for (int b = 0; b < ND; ++b) acc[b] = (f32x16){};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // row of V^T that MFMA row r reads, so each lane ends with 16 consecutive
-  // output features: d = 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3)
-  const int vrow = 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);
-
+  // One key tile: tile j sits in LDS buffer BUF (= j & 1, a compile-time
+  // constant so every LDS address is a per-lane base plus an immediate); MASK
+  // marks the ragged last tile, the only one that needs keys >= N masked.
   const int ntiles = (N + kBC - 1) / kBC;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < ntiles) load_tile(j + 1);
+  auto step = [&](auto buf_c, auto mask_c, int j) {
+    constexpr int BUF = decltype(buf_c)::value;
+    constexpr bool MASK = decltype(mask_c)::value;
+    if (j + 1 < ntiles) load_tile(j + 1, BUF ^ 1);
+    const uint16_t* Kb = Ks[BUF];
+    const uint16_t* Vb = Vs[BUF];
 
     // S^T (keys x queries) for two 32-key blocks
     f32x16 s[2] = {(f32x16){}, (f32x16){}};
@@ -134,12 +166,11 @@ __global__ __launch_bounds__(256, 2) void anchor_bf16(const uint16_t* __restrict
     for (int t = 0; t < NK; ++t) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(&Ks[buf][(kb * 32 + r) * KS + 16 * t + 8 * h]);
+        const u32x4 a = *reinterpret_cast<const u32x4*>(&Kb[kb * 32 * D + koff[t]]);
         s[kb] = mfma32x32x16(a, qf[t], s[kb]);
       }
     }
-    // keys past N in the last tile
-    if ((j + 1) * kBC > N) {
+    if (MASK) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -157,6 +188,9 @@ __global__ __launch_bounds__(256, 2) void anchor_bf16(const uint16_t* __restrict
     mt = fmaxf(mt, swap_halves(mt)) * c;
     const bool need = mt > m_run + kTau;
     if (__any(need)) {
+      // a real branch: the empty volatile asm keeps the compiler from turning
+      // this rarely taken rescale into straight-line code run on every tile
+      asm volatile("");
       const float m_new = need ? mt : m_run;
       const float alpha = exp2_fast(m_run - m_new);
       l_run *= alpha;
@@ -164,38 +198,58 @@ __global__ __launch_bounds__(256, 2) void anchor_bf16(const uint16_t* __restrict
       for (int b = 0; b < ND; ++b) acc[b] *= alpha;
       m_run = m_new;
     }
-    // P = 2^(s*c - m), row sum, pack to bf16 B operands (4 k-steps of 16 keys)
+    // P = 2^(s*c - m) packed to bf16 B operands (4 k-steps of 16 keys); the row
+    // sum adds the same rounded values the MFMA consumes
     u32x4 pb[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       float p[16];
 #pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        p[x] = exp2_fast(fmaf(s[kb][x], c, -m_run));
-        l_run += p[x];
-      }
+      for (int x = 0; x < 16; ++x) p[x] = exp2_fast(fmaf(s[kb][x], c, -m_run));
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const int qq = half * 2;
-        pb[kb * 2 + half] = (u32x4){pack_bf16(p[qq * 4 + 0], p[qq * 4 + 1]),
-                                    pack_bf16(p[qq * 4 + 2], p[qq * 4 + 3]),
-                                    pack_bf16(p[qq * 4 + 4], p[qq * 4 + 5]),
-                                    pack_bf16(p[qq * 4 + 6], p[qq * 4 + 7])};
+        const int qq = half * 8;
+        pb[kb * 2 + half] = (u32x4){pack_bf16(p[qq + 0], p[qq + 1]), pack_bf16(p[qq + 2], p[qq + 3]),
+                                    pack_bf16(p[qq + 4], p[qq + 5]), pack_bf16(p[qq + 6], p[qq + 7])};
       }
     }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) l_run = add_bf16x2(pb[ks][x], l_run);
     // O^T += V^T P^T; k-slot s of half h is key 16ks + 8(s>>2) + 4h + (s&3)
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int b = 0; b < ND; ++b) {
-        const uint16_t* vp = &Vt[buf][(b * 32 + vrow) * VS + ks * 16 + 4 * h];
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vp);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vp + 8);
+        const u32x2 lo = lds_read_tr16(&Vb[ks * 16 * D + voff[b]]);
+        const u32x2 hi = lds_read_tr16(&Vb[(ks * 16 + 8) * D + voff[b]]);
         acc[b] = mfma32x32x16((u32x4){lo[0], lo[1], hi[0], hi[1]}, pb[ks], acc[b]);
       }
     }
-    if (j + 1 < ntiles) store_tile(buf ^ 1);
+    wait_all_memory();  // tile j + 1 has landed in LDS
     __syncthreads();
+  };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  using Full = std::false_type;
+  using Ragged = std::true_type;
+
+  load_tile(0, 0);
+  wait_all_memory();
+  __syncthreads();
+  const int nfull = N / kBC;
+  int j = 0;
+  for (; j + 2 <= nfull; j += 2) {
+    step(B0{}, Full{}, j);
+    step(B1{}, Full{}, j + 1);
+  }
+  if (j < nfull) {
+    step(B0{}, Full{}, j);
+    ++j;
+    if (j < ntiles) step(B1{}, Ragged{}, j);
+  } else if (j < ntiles) {
+    step(B0{}, Ragged{}, j);
   }
 
   // epilogue: lane (query r, half h) holds features 32b + 16h + 0..15 of block b

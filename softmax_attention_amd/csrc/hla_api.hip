@@ -46,7 +46,8 @@ hla_status check_dims(const hla_dims* d) {
   if (d->B > kMaxIndex || d->H > kMaxIndex || d->N > kMaxIndex) return HLA_ERR_BAD_SHAPE;
   const int64_t bh = d->B * d->H;  // < 2^62, no overflow
   if (bh > 65535 * 1024LL) return HLA_ERR_BAD_SHAPE;
-  if (d->N * d->D > kMaxIndex) return HLA_ERR_BAD_SHAPE;
+  // per-head byte offsets are 32-bit (buffer loads), with room for one tile past N
+  if (d->N * d->D > kMaxIndex - 65536) return HLA_ERR_BAD_SHAPE;
   if (bh > 0 && d->N * d->D > INT64_MAX / 4 / bh) return HLA_ERR_BAD_SHAPE;
   // anchor grid: B*H * ceil(N/128) workgroups in one dimension
   if (bh * ((d->N + 127) / 128) > kMaxIndex) return HLA_ERR_BAD_SHAPE;

@@ -66,6 +66,53 @@ __device__ __forceinline__ float swap_halves(float x) {
   return __shfl_xor(x, 32, 64);
 }
 
+// Raw buffer access: a 32-bit byte offset from a per-tensor base; reads past
+// num_bytes return 0 and never touch memory. Resource word 3 is the gfx9-family
+// raw-buffer format (32-bit data format, no swizzle).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t num_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_bytes,
+                                           0x00020000);
+}
+// Same, for a base and size the compiler cannot prove wave-uniform although
+// they are (readfirstlane keeps the descriptor in scalar registers).
+__device__ __forceinline__ rsrc_t make_rsrc_uniform(const void* base, uint32_t num_bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint32_t n = __builtin_amdgcn_readfirstlane(num_bytes);
+  return make_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo), n);
+}
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
+}
+
+// 16 bytes per lane from a raw buffer straight into LDS: lane i of the wave
+// writes lds_base + 16 i (lds_base is wave-uniform); past num_bytes it writes 0.
+__device__ __forceinline__ void buf_load16_lds(rsrc_t r, uint32_t byte_off, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16,
+                                           (int)byte_off, 0, 0, 0);
+}
+
+// Wait until every outstanding memory operation of this wave has completed.
+__device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
+
+// LDS transpose read (ds_read_b64_tr_b16): within each group of 16 lanes, lane j
+// receives element (j % 4) of the 8-byte rows that lanes 4e + j/4 (e = 0..3)
+// point at, as its elements e = 0..3.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* lds_elem) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_elem));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// Row sum helper: a + lo(p) + hi(p) for a packed bf16 pair p (v_dot2 with ones).
+__device__ __forceinline__ float add_bf16x2(uint32_t p, float a) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p),
+                                         (bf16x2){(__bf16)1.0f, (__bf16)1.0f}, a, false);
+}
+
 __device__ __forceinline__ u32x4 ldg16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void stg16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 

@@ -156,6 +156,7 @@ def main():
     sets = [gpu_inputs(w, s, torch) for s in range(2)]
     outs = [torch.empty_like(sets[0][0]) for _ in range(2)]
     ws = hla.linear_workspace(sets[0][0])
+    ws_a = hla.anchor_workspace(sets[0][0])
 
     def linear(i):
         q, k, v, g = sets[i % 2]
@@ -163,7 +164,7 @@ def main():
 
     def anchor(i):
         q, k, v, g = sets[i % 2]
-        hla.hla_softmax_anchor_fwd(q, k, v, g, out=outs[1], scale=w.scale)
+        hla.hla_softmax_anchor_fwd(q, k, v, g, out=outs[1], scale=w.scale, workspace=ws_a)
 
     if args.profile:
         fn = {"anchor": [anchor], "linear": [linear], "step": [linear, anchor]}[args.profile]
@@ -251,7 +252,7 @@ def stack_timing(torch, hla):
     gen = torch.Generator(device="cuda")
     gen.manual_seed(20261203 + 1000 * w.index + 4)
     x = torch.randn((w.B, w.H, w.N, w.D), generator=gen, device="cuda", dtype=torch.float32)
-    ws = hla.linear_workspace(layers[0][0], torch.float32)
+    ws = hla.stack_workspace(layers[0][0], [0, 1], torch.float32)
     res = {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D}
     for name, kinds in (("hybrid_3to1", list(w.kinds)), ("all_softmax", [1] * 8)):
         hla.hla_hybrid_stack_fwd(x, layers, kinds, eps=w.eps, scale=w.scale, workspace=ws)

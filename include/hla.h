@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define HLA_ABI_VERSION 1
+#define HLA_ABI_VERSION 2
 
 typedef enum { HLA_F32 = 0, HLA_BF16 = 1 } hla_dtype;
 
@@ -96,14 +96,21 @@ hla_status hla_linear_fwd(const hla_dims* d, const void* q, const void* k, const
                           const void* g, void* out, int accumulate, float eps, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace hla_softmax_anchor_fwd needs for `d`: on the bf16
+ * path a repacked copy of V (B*H*D*ceil(N/64)*64 bf16, V transposed with zero
+ * keys past N); 0 on the fp32 path. Host-only and pure; 0 for invalid or
+ * unsupported dims and for empty tensors. */
+size_t hla_softmax_anchor_workspace_bytes(const hla_dims* d);
+
 /* Gated softmax anchor (non-causal, no mask, no positional term) -- the periodic
  * gated-softmax layer that restores exact token interactions (SANA-Video 2.0
  * abstract; lode.cx article, "The Core Innovation"). scale must be finite and
- * > 0 (1/sqrt(D) is the usual choice). accumulate as in hla_linear_fwd. Needs
- * no workspace. */
+ * > 0 (1/sqrt(D) is the usual choice). accumulate as in hla_linear_fwd.
+ * `workspace` is a device buffer of at least hla_softmax_anchor_workspace_bytes(d)
+ * bytes (may be NULL when that is 0); its contents on entry do not matter. */
 hla_status hla_softmax_anchor_fwd(const hla_dims* d, const void* q, const void* k, const void* v,
                                   const void* g, void* out, int accumulate, float scale,
-                                  void* stream);
+                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /* Hybrid stack: for l = 0 .. n_layers-1 in order, x += layer_l(q[l], k[l], v[l], g[l])
  * where kinds[l] is HLA_LAYER_LINEAR or HLA_LAYER_SOFTMAX; SANA-Video 2.0 places a
@@ -112,9 +119,9 @@ hla_status hla_softmax_anchor_fwd(const hla_dims* d, const void* q, const void* 
  * d->out_dtype and is updated in place (an fp32 x keeps the residual stream
  * exact to fp32 rounding). kinds, q, k, v, g are host arrays of n_layers
  * entries; each q[l] ... g[l] is a device tensor like those of hla_linear_fwd.
- * workspace as for hla_linear_fwd (needed only when some kind is linear; it
- * may be NULL with workspace_bytes 0 otherwise). All layers are enqueued on
- * `stream` in order. */
+ * workspace must hold max(hla_linear_workspace_bytes(d) if some kind is linear,
+ * hla_softmax_anchor_workspace_bytes(d) if some kind is softmax) bytes; layers
+ * reuse it one after another. All layers are enqueued on `stream` in order. */
 hla_status hla_hybrid_stack_fwd(const hla_dims* d, int n_layers, const int32_t* kinds,
                                 const void* const* q, const void* const* k,
                                 const void* const* v, const void* const* g, void* x, float eps,

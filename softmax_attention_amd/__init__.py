@@ -5,8 +5,8 @@ A thin ctypes layer over the C ABI in include/hla.h, with the same names:
 ``hla_linear_workspace_bytes``, ``hla_status_str``, ``hla_abi_version``. It only
 marshals arguments: torch tensors become device pointers and the current torch
 stream becomes the HIP stream; every step of the computation runs in the HIP
-kernels. The shared library must have been built (``python -m
-softmax_attention_amd.build``); importing this package without it raises.
+kernels. The shared library must have been built (``python
+softmax_attention_amd/build.py``); importing this package without it raises.
 """
 from __future__ import annotations
 
@@ -27,7 +27,7 @@ STATUS = {
     4: "HLA_ERR_BAD_ARG", 5: "HLA_ERR_ALIGN", 6: "HLA_ERR_WORKSPACE", 7: "HLA_ERR_HIP",
 }
 EXPORTS = ("hla_abi_version", "hla_status_str", "hla_linear_workspace_bytes", "hla_linear_fwd",
-           "hla_softmax_anchor_fwd", "hla_hybrid_stack_fwd")
+           "hla_softmax_anchor_workspace_bytes", "hla_softmax_anchor_fwd", "hla_hybrid_stack_fwd")
 
 
 class hla_dims(ctypes.Structure):
@@ -54,7 +54,7 @@ def hip_runtimes_loaded() -> list:
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m softmax_attention_amd.build`")
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python softmax_attention_amd/build.py`")
     # torch ships its own HIP runtime. Load it first so that libhla binds to that
     # same runtime (same soname) instead of pulling in a second copy from
     # /opt/rocm: device memory and streams come from torch, and two runtimes in
@@ -75,8 +75,11 @@ def _load() -> ctypes.CDLL:
     lib.hla_linear_fwd.restype = ctypes.c_int
     lib.hla_linear_fwd.argtypes = [pd, P, P, P, P, P, ctypes.c_int, ctypes.c_float, P,
                                    ctypes.c_size_t, P]
+    lib.hla_softmax_anchor_workspace_bytes.restype = ctypes.c_size_t
+    lib.hla_softmax_anchor_workspace_bytes.argtypes = [pd]
     lib.hla_softmax_anchor_fwd.restype = ctypes.c_int
-    lib.hla_softmax_anchor_fwd.argtypes = [pd, P, P, P, P, P, ctypes.c_int, ctypes.c_float, P]
+    lib.hla_softmax_anchor_fwd.argtypes = [pd, P, P, P, P, P, ctypes.c_int, ctypes.c_float, P,
+                                           ctypes.c_size_t, P]
     lib.hla_hybrid_stack_fwd.restype = ctypes.c_int
     lib.hla_hybrid_stack_fwd.argtypes = [pd, ctypes.c_int, ctypes.POINTER(ctypes.c_int32),
                                          ctypes.POINTER(P), ctypes.POINTER(P), ctypes.POINTER(P),
@@ -156,12 +159,33 @@ def hla_linear_workspace_bytes(dims: hla_dims) -> int:
     return int(lib.hla_linear_workspace_bytes(ctypes.byref(dims)))
 
 
+def hla_softmax_anchor_workspace_bytes(dims: hla_dims) -> int:
+    return int(lib.hla_softmax_anchor_workspace_bytes(ctypes.byref(dims)))
+
+
+def _workspace(nbytes: int, device):
+    return _torch().empty(max(int(nbytes), 256), dtype=_torch().uint8, device=device)
+
+
 def linear_workspace(q, out_dtype=None):
-    """A device workspace tensor sized for hla_linear_fwd / hla_hybrid_stack_fwd on q's shape."""
-    torch = _torch()
+    """A device workspace tensor sized for hla_linear_fwd on q's shape."""
+    return _workspace(hla_linear_workspace_bytes(dims_of(q, out_dtype)), q.device)
+
+
+def anchor_workspace(q, out_dtype=None):
+    """A device workspace tensor sized for hla_softmax_anchor_fwd on q's shape."""
+    return _workspace(hla_softmax_anchor_workspace_bytes(dims_of(q, out_dtype)), q.device)
+
+
+def stack_workspace(q, kinds, out_dtype=None):
+    """A device workspace tensor sized for hla_hybrid_stack_fwd with these layer kinds."""
     d = dims_of(q, out_dtype)
-    n = hla_linear_workspace_bytes(d)
-    return torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
+    n = 0
+    if any(k == HLA_LAYER_LINEAR for k in kinds):
+        n = max(n, hla_linear_workspace_bytes(d))
+    if any(k == HLA_LAYER_SOFTMAX for k in kinds):
+        n = max(n, hla_softmax_anchor_workspace_bytes(d))
+    return _workspace(n, q.device)
 
 
 def hla_linear_fwd(q, k, v, g, out=None, accumulate: bool = False, eps: float = 1e-6,
@@ -183,7 +207,7 @@ def hla_linear_fwd(q, k, v, g, out=None, accumulate: bool = False, eps: float = 
 
 
 def hla_softmax_anchor_fwd(q, k, v, g, out=None, accumulate: bool = False,
-                           scale: Optional[float] = None, stream=None):
+                           scale: Optional[float] = None, workspace=None, stream=None):
     """Gated softmax anchor O = sigma(G) * softmax(scale Q K^T) V; returns out."""
     torch = _torch()
     _check(q, k, v, g)
@@ -192,9 +216,12 @@ def hla_softmax_anchor_fwd(q, k, v, g, out=None, accumulate: bool = False,
     _check(q, out)
     d = dims_of(q, out.dtype)
     scale = 1.0 / math.sqrt(q.shape[-1]) if scale is None else float(scale)
+    if workspace is None:
+        workspace = anchor_workspace(q, out.dtype)
     st = lib.hla_softmax_anchor_fwd(ctypes.byref(d), q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                     g.data_ptr(), out.data_ptr(), int(bool(accumulate)), scale,
-                                    _stream(stream))
+                                    workspace.data_ptr(),
+                                    workspace.numel() * workspace.element_size(), _stream(stream))
     _raise("hla_softmax_anchor_fwd", st)
     return out
 
@@ -211,8 +238,8 @@ def hla_hybrid_stack_fwd(x, layers: Sequence, kinds: Sequence[int], eps: float =
     q0 = layers[0][0]
     d = dims_of(q0, x.dtype)
     scale = 1.0 / math.sqrt(q0.shape[-1]) if scale is None else float(scale)
-    if workspace is None and any(kd == HLA_LAYER_LINEAR for kd in kinds):
-        workspace = linear_workspace(q0, x.dtype)
+    if workspace is None:
+        workspace = stack_workspace(q0, kinds, x.dtype)
     arr = ctypes.c_void_p * n
     qs = arr(*[l[0].data_ptr() for l in layers])
     ks = arr(*[l[1].data_ptr() for l in layers])

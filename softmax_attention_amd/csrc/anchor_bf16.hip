@@ -35,33 +35,82 @@ constexpr int kBR = 128;  // query rows per workgroup
 constexpr int kBC = 64;   // keys per LDS tile
 constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
 
-// LDS tiles are row-major (one key per row) with XOR swizzles of whole chunks
-// instead of padding:
-//   K: 16-byte chunk c of row k sits at chunk c ^ (k & 15) (c ^ (k & 7) for D=64),
-//      so the 32 rows one S^T operand read touches spread over all banks;
-//   V: 8-byte chunk c of row k sits at chunk c ^ kVx[k & 3], which keeps the
-//      transposed (ds_read_b64_tr_b16) operand reads of 16 lanes on 16 distinct
-//      bank pairs.
+// LDS tiles use XOR swizzles of whole 16-byte chunks instead of padding:
+//   K   (row = key, D/8 chunks): chunk c of row k sits at c ^ (k & 15)
+//       (c ^ (k & 7) for D=64), so the 32 rows one S^T operand read touches
+//       spread over all banks;
+//   V^T (row = feature, 8 chunks of 8 keys): chunk c of row d sits at
+//       c ^ vt_swz(d), which puts the 16 rows one P V operand read touches on
+//       16 distinct bank groups.
 template <int D>
 struct AnchorSwz;
 template <>
 struct AnchorSwz<128> {
   static constexpr int kmask = 15;
-  __device__ static int vx8(int k) { return (0x18120a00 >> (8 * (k & 3))) & 0xff; }  // 0,10,18,24
 };
 template <>
 struct AnchorSwz<64> {
   static constexpr int kmask = 7;
-  __device__ static int vx8(int k) { return (0x08020a00 >> (8 * (k & 3))) & 0xff; }  // 0,10,2,8
 };
+__device__ __forceinline__ int vt_swz(int d) { return ((d >> 1) & 3) | ((d >> 2) & 4); }
+
+// Position of key k16 (0..15) of a 16-key group in the repacked V^T rows: MFMA
+// lane half h takes k-slots s = 0..7 = keys 4h + (s & 3) + 8 (s >> 2), so the
+// group is stored as [keys 0-3, 8-11 | keys 4-7, 12-15] and each half reads
+// its 8 keys as one 16-byte chunk.
+__device__ __forceinline__ int vt_pos(int k16) { return 8 * ((k16 >> 2) & 1) + 4 * (k16 >> 3) + (k16 & 3); }
+
+// ---------------------------------------------------------------------------
+// V -> V^T repack (once per call): per head, V^T[d][n_pad] with the key order
+// of vt_pos inside every 16-key group and zeros for keys >= N.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void anchor_pack_vt(const uint16_t* __restrict__ V,
+                                                      uint16_t* __restrict__ VT, int N,
+                                                      int n_pad) {
+  constexpr int CH = D / 8;
+  __shared__ uint32_t tile[64][D / 2 + 1];  // 64 keys x D features, odd word stride
+  const int j = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const uint16_t* Vh = V + (size_t)bh * N * D;
+  uint16_t* VTh = VT + (size_t)bh * D * n_pad;
+  for (int c = tid; c < 64 * CH; c += 256) {
+    const int key = c / CH, col = (c % CH) * 8, n = j * 64 + key;
+    const u32x4 v = n < N ? ldg16(Vh + (size_t)n * D + col) : (u32x4){0, 0, 0, 0};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) tile[key][col / 2 + p] = v[p];
+  }
+  __syncthreads();
+  // output: D rows x 8 chunks of 8 keys; chunk pc holds positions 8pc..8pc+7
+  for (int c = tid; c < D * 8; c += 256) {
+    const int d = c >> 3, pc = c & 7;
+    uint32_t w[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      uint32_t e[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int pos = 8 * pc + 2 * p + u;           // position within the tile
+        const int g16 = pos >> 4, r = pos & 15;       // group, position in group
+        // invert vt_pos: r = 8h + 4(k>>3) + (k&3) -> k = 4h + 8(r>>2 & 1) + (r&3)
+        const int k16 = 4 * (r >> 3) + 8 * ((r >> 2) & 1) + (r & 3);
+        const uint32_t word = tile[g16 * 16 + k16][d >> 1];
+        e[u] = (d & 1) ? (word >> 16) : (word & 0xffffu);
+      }
+      w[p] = e[0] | (e[1] << 16);
+    }
+    stg16(VTh + (size_t)d * n_pad + j * 64 + pc * 8, (u32x4){w[0], w[1], w[2], w[3]});
+  }
+}
 
 template <int D, bool OUT_F32>
 __global__ __launch_bounds__(256, 2) void anchor_bf16(const uint16_t* __restrict__ Q,
                                                       const uint16_t* __restrict__ K,
                                                       const uint16_t* __restrict__ V,
                                                       const uint16_t* __restrict__ G,
-                                                      void* __restrict__ out, int N, int nqb,
-                                                      int total, float c, int accumulate) {
+                                                      const uint16_t* __restrict__ VT,
+                                                      void* __restrict__ out, int N, int n_pad,
+                                                      int nqb, int total, float c,
+                                                      int accumulate) {
   constexpr int NK = D / 16;              // k-steps of S^T
   constexpr int ND = D / 32;              // 32-row blocks of O^T
   constexpr int CH = D / 8;               // 16-byte chunks per row
@@ -99,69 +148,65 @@ __global__ __launch_bounds__(256, 2) void anchor_bf16(const uint16_t* __restrict
   }
 
   // Tiles go global -> LDS directly (buffer_load ... lds): instruction i of
-  // wave w fills the 1 KB LDS block bw = LOADS*w + i, i.e. rows 4bw..4bw+3 with
-  // lane l at row 4bw + l/16, physical 16-byte chunk l%16. Each lane fetches
-  // the logical chunk that the swizzle puts there.
-  constexpr int ROWS_PER_BLK = 1024 / (D * 2);   // 4 rows of 256 B (8 for D=64)
+  // wave w fills the 1 KB LDS block bw = LOADS*w + i in lane order. K tiles hold
+  // 4 key rows of 256 B per block (8 of 128 B for D=64): lane l lands in row
+  // 4bw + l/16, physical chunk l%16. V^T tiles hold 8 feature rows of 128 B (64
+  // keys) per block: lane l lands in row 8bw + l/8, physical chunk l%8. Each lane
+  // fetches the logical chunk that the swizzle puts there.
+  constexpr int ROWS_PER_BLK = 1024 / (D * 2);
   uint32_t goff_k[LOADS], goff_v[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int blk = LOADS * wave + i;
     const int row = blk * ROWS_PER_BLK + lane / CH, pc = lane % CH;
-    const int ck = pc ^ (row & Swz::kmask);
-    const int cv = (2 * pc ^ Swz::vx8(row)) / 2;
-    goff_k[i] = (row * D + ck * 8) * 2;
-    goff_v[i] = (row * D + cv * 8) * 2;
+    goff_k[i] = (row * D + ((pc ^ (row & Swz::kmask)) * 8)) * 2;
+    const int vd = blk * 8 + (lane >> 3), vpc = lane & 7;
+    goff_v[i] = ((uint32_t)vd * n_pad + ((vpc ^ vt_swz(vd)) * 8)) * 2;
   }
-  // issue tile j into LDS buffer buf (completion: wait_all_memory + barrier)
-  auto load_tile = [&](int j, int buf) {
+  const uint32_t vt_head_bytes = (uint32_t)D * n_pad * 2;
+  // issue K (or V^T) tile j into LDS buffer buf (completion: wait_all_memory + barrier)
+  auto load_k = [&](int j, int buf) {
     const uint32_t done = (uint32_t)j * kTileBytes;
     const uint32_t left = done < head_bytes ? head_bytes - done : 0u;
     const rsrc_t kr = make_rsrc_uniform(K + base + (size_t)j * kBC * D, left);
-    const rsrc_t vr = make_rsrc_uniform(V + base + (size_t)j * kBC * D, left);
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int blk = LOADS * wave + i;
-      buf_load16_lds(kr, goff_k[i], &Ks[buf][blk * 512]);
-      buf_load16_lds(vr, goff_v[i], &Vs[buf][blk * 512]);
-    }
+    for (int i = 0; i < LOADS; ++i) buf_load16_lds(kr, goff_k[i], &Ks[buf][(LOADS * wave + i) * 512]);
+  };
+  auto load_v = [&](int j, int buf) {
+    const uint32_t done = (uint32_t)j * kBC * 2;
+    const uint32_t left = j * kBC < n_pad ? vt_head_bytes - done : 0u;
+    const rsrc_t vr = make_rsrc_uniform(VT + (size_t)bh * D * n_pad + (size_t)j * kBC, left);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) buf_load16_lds(vr, goff_v[i], &Vs[buf][(LOADS * wave + i) * 512]);
   };
 
   // S^T operand A (key rows): lane reads row kb*32 + r, chunk 2t + h (swizzled)
   int koff[NK];
 #pragma unroll
   for (int t = 0; t < NK; ++t) koff[t] = r * D + (((2 * t + h) ^ (r & Swz::kmask)) * 8);
-  // O^T operand A (V^T) through transposed reads: source lane (e = (lane>>2)&3,
-  // q = lane&3) of each 16-lane group points at key 4h + e (+16 ks, +8 for the
-  // upper four k-slots) and at the 4 features of output rows R = 16 g + 4 q..+3,
-  // where MFMA row R maps to feature 16((R>>2)&1) + 4(R>>3) + (R&3) of block b.
-  const int ve = (lane >> 2) & 3, vq = lane & 3, vg = (lane >> 4) & 1;
-  const int vkey = 4 * h + ve;
-  int voff[ND];
+  // O^T operand A (V^T rows): MFMA row r of block b is feature
+  // d = 32b + vrow, vrow = 16((r>>2)&1) + 4(r>>3) + (r&3), so each lane ends with
+  // 16 consecutive output features; its 8 keys of k-step ks are logical chunk
+  // 2ks + h of that row
+  const int vrow = 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);
+  int voff[4];
 #pragma unroll
-  for (int b = 0; b < ND; ++b) {
-    const int chunk8 = b * 8 + 4 * (vq & 1) + (vq >> 1) + 2 * vg;
-    voff[b] = vkey * D + ((chunk8 ^ Swz::vx8(vkey)) * 4);
-  }
+  for (int ks = 0; ks < 4; ++ks) voff[ks] = vrow * kBC + (((2 * ks + h) ^ vt_swz(vrow)) * 8);
 
   f32x16 acc[ND];
 #pragma unroll
   for (int b = 0; b < ND; ++b) acc[b] = (f32x16){};
   float m_run = -INFINITY, l_run = 0.f;
-
-  // One key tile: tile j sits in LDS buffer BUF (= j & 1, a compile-time
-  // constant so every LDS address is a per-lane base plus an immediate); MASK
-  // marks the ragged last tile, the only one that needs keys >= N masked.
   const int ntiles = (N + kBC - 1) / kBC;
-  auto step = [&](auto buf_c, auto mask_c, int j) {
-    constexpr int BUF = decltype(buf_c)::value;
-    constexpr bool MASK = decltype(mask_c)::value;
-    if (j + 1 < ntiles) load_tile(j + 1, BUF ^ 1);
-    const uint16_t* Kb = Ks[BUF];
-    const uint16_t* Vb = Vs[BUF];
+  const bool ragged = (N % kBC) != 0;
 
-    // S^T (keys x queries) for two 32-key blocks
-    f32x16 s[2] = {(f32x16){}, (f32x16){}};
+  // ---- building blocks -----------------------------------------------------
+  // S^T of the tile held in K buffer KB (two 32-key blocks)
+  auto s_tile = [&](auto kb_c, f32x16* s) {
+    constexpr int KB = decltype(kb_c)::value;
+    const uint16_t* Kb = Ks[KB];
+    s[0] = (f32x16){};
+    s[1] = (f32x16){};
 #pragma unroll
     for (int t = 0; t < NK; ++t) {
 #pragma unroll
@@ -170,7 +215,33 @@ __global__ __launch_bounds__(256, 2) void anchor_bf16(const uint16_t* __restrict
         s[kb] = mfma32x32x16(a, qf[t], s[kb]);
       }
     }
-    if (MASK) {
+  };
+  // O^T += V^T P^T for the tile held in V buffer VB; k-slot s of half h is
+  // key 16ks + 8(s>>2) + 4h + (s&3)
+  auto pv_tile = [&](auto vb_c, const u32x4* pb) {
+    constexpr int VB = decltype(vb_c)::value;
+    const uint16_t* Vb = Vs[VB];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int b = 0; b < ND; ++b) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(&Vb[b * 32 * kBC + voff[ks]]);
+        acc[b] = mfma32x32x16(a, pb[ks], acc[b]);
+      }
+    }
+  };
+  // issue loads: K tile jk into K buffer kw, V tile jv into V buffer vw. No
+  // branch: a tile past the end gets a zero-size descriptor, so its loads
+  // touch no memory and fill LDS with zeros that nothing reads.
+  auto issue = [&](int jk, int kw, int jv, int vw) {
+    load_k(jk, kw);
+    load_v(jv, vw);
+  };
+  // online softmax of S^T for tile j: returns the bf16 P^T operands in pb and
+  // the factor alpha by which the accumulator must be rescaled (1 if none)
+  auto softmax = [&](f32x16* s, u32x4* pb, int j, bool mask) -> float {
+    if (mask) {
+      asm volatile("");
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -179,28 +250,20 @@ __global__ __launch_bounds__(256, 2) void anchor_bf16(const uint16_t* __restrict
           if (key >= N) s[kb][x] = -INFINITY;
         }
     }
-    // row max over this tile (own 32 scores, then the partner lane's)
-    float mt = s[0][0];
+    // row max: a tree (short dependency chains), then the partner half-wave
+    float m16[16];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int x = 0; x < 16; ++x) m16[x] = fmaxf(s[0][x], s[1][x]);
 #pragma unroll
-      for (int x = 0; x < 16; ++x) mt = fmaxf(mt, s[kb][x]);
-    mt = fmaxf(mt, swap_halves(mt)) * c;
+    for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+      for (int x = 0; x < w; ++x) m16[x] = fmaxf(m16[x], m16[x + w]);
+    const float mt = max_halves(m16[0]) * c;
     const bool need = mt > m_run + kTau;
-    if (__any(need)) {
-      // a real branch: the empty volatile asm keeps the compiler from turning
-      // this rarely taken rescale into straight-line code run on every tile
-      asm volatile("");
-      const float m_new = need ? mt : m_run;
-      const float alpha = exp2_fast(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int b = 0; b < ND; ++b) acc[b] *= alpha;
-      m_run = m_new;
-    }
-    // P = 2^(s*c - m) packed to bf16 B operands (4 k-steps of 16 keys); the row
-    // sum adds the same rounded values the MFMA consumes
-    u32x4 pb[4];
+    const float m_new = need ? mt : m_run;
+    const float alpha = exp2_fast(m_run - m_new);  // 1 unless the max moved up
+    m_run = m_new;
+    l_run *= alpha;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       float p[16];
@@ -213,47 +276,97 @@ __global__ __launch_bounds__(256, 2) void anchor_bf16(const uint16_t* __restrict
                                     pack_bf16(p[qq + 4], p[qq + 5]), pack_bf16(p[qq + 6], p[qq + 7])};
       }
     }
+    // the row sum adds the same rounded values the MFMA consumes (4 chains)
+    float l4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int x = 0; x < 4; ++x)
 #pragma unroll
-      for (int x = 0; x < 4; ++x) l_run = add_bf16x2(pb[ks][x], l_run);
-    // O^T += V^T P^T; k-slot s of half h is key 16ks + 8(s>>2) + 4h + (s&3)
+      for (int ks = 0; ks < 4; ++ks) l4[ks] = add_bf16x2(pb[ks][x], l4[ks]);
+    l_run += (l4[0] + l4[1]) + (l4[2] + l4[3]);
+    return alpha;
+  };
+  auto rescale = [&](float alpha) {
+    // a real branch: the empty volatile asm keeps the compiler from turning
+    // this rarely taken rescale into straight-line code run on every tile
+    if (__any(alpha != 1.0f)) {
+      asm volatile("");
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-      for (int b = 0; b < ND; ++b) {
-        const u32x2 lo = lds_read_tr16(&Vb[ks * 16 * D + voff[b]]);
-        const u32x2 hi = lds_read_tr16(&Vb[(ks * 16 + 8) * D + voff[b]]);
-        acc[b] = mfma32x32x16((u32x4){lo[0], lo[1], hi[0], hi[1]}, pb[ks], acc[b]);
-      }
+      for (int b = 0; b < ND; ++b) acc[b] *= alpha;
     }
-    wait_all_memory();  // tile j + 1 has landed in LDS
+  };
+
+  // ---- software pipeline ------------------------------------------------------
+  // Iteration j overlaps the softmax of tile j (VALU) with the MFMAs of P V for
+  // tile j-1 and of S^T for tile j+1, which do not depend on it. K therefore
+  // runs one tile ahead of the softmax and V one tile behind: iteration j reads
+  // K(j+1) from K buffer (j+1)&1 and V(j-1) from V buffer (j-1)&1 while K(j+2)
+  // and V(j) stream into buffers j&1. The accumulator rescale for tile j waits
+  // until P V of tile j-1 has been added.
+  f32x16 s_cur[2];
+  u32x4 p_prev[4];
+  auto iteration = [&](auto buf_c, auto steady_c, int j) {
+    constexpr int BUF = decltype(buf_c)::value;
+    constexpr bool STEADY = decltype(steady_c)::value;
+    using Cur = std::integral_constant<int, BUF>;
+    using Oth = std::integral_constant<int, BUF ^ 1>;
+    // S(j) was computed last iteration; re-define it here (an empty asm, no
+    // memory access) so the compiler cannot hoist this iteration's softmax
+    // above the previous barrier, away from the MFMAs it should overlap
+    asm volatile("" : "+v"(s_cur[0]), "+v"(s_cur[1]));
+    issue(j + 2, BUF, j, BUF);
+    u32x4 p_cur[4];
+    const bool mask = !STEADY && ragged && j == ntiles - 1;
+    const float alpha = softmax(s_cur, p_cur, j, mask);
+    if (STEADY || j > 0) pv_tile(Oth{}, p_prev);
+    f32x16 s_next[2];
+    if (STEADY || j + 1 < ntiles) s_tile(Oth{}, s_next);
+    // and keep P(j) and the row sum from sinking below them: they are used by
+    // the next iteration only, so the compiler would otherwise compute them late
+    asm volatile("" ::"v"(p_cur[0]), "v"(p_cur[1]), "v"(p_cur[2]), "v"(p_cur[3]), "v"(l_run));
+    rescale(alpha);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) p_prev[ks] = p_cur[ks];
+    s_cur[0] = s_next[0];
+    s_cur[1] = s_next[1];
+    wait_all_memory();  // this iteration's tiles have landed in LDS
     __syncthreads();
+    // keep the next iteration's softmax out of this one: it must stay next to
+    // the MFMAs it is meant to overlap
+    __builtin_amdgcn_sched_barrier(0);
   };
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
-  using Full = std::false_type;
-  using Ragged = std::true_type;
+  using Steady = std::true_type;
+  using Edge = std::false_type;
 
-  load_tile(0, 0);
+  // prologue: K(0), K(1) in; S^T of tile 0
+  load_k(0, 0);
+  if (ntiles > 1) load_k(1, 1);
   wait_all_memory();
   __syncthreads();
-  const int nfull = N / kBC;
-  int j = 0;
-  for (; j + 2 <= nfull; j += 2) {
-    step(B0{}, Full{}, j);
-    step(B1{}, Full{}, j + 1);
+  s_tile(B0{}, s_cur);
+  __syncthreads();  // K buffer 0 is free for K(2)
+
+  iteration(B0{}, Edge{}, 0);
+  int j = 1;
+  for (; j + 2 <= ntiles - 1; j += 2) {  // tiles 1 .. ntiles-2 are steady
+    iteration(B1{}, Steady{}, j);
+    iteration(B0{}, Steady{}, j + 1);
   }
-  if (j < nfull) {
-    step(B0{}, Full{}, j);
+  if (j <= ntiles - 2) {
+    iteration(B1{}, Steady{}, j);
     ++j;
-    if (j < ntiles) step(B1{}, Ragged{}, j);
-  } else if (j < ntiles) {
-    step(B0{}, Ragged{}, j);
   }
+  if (j == ntiles - 1 && j > 0) {  // the last tile
+    if (j & 1) iteration(B1{}, Edge{}, j);
+    else iteration(B0{}, Edge{}, j);
+  }
+  // P V of the last tile
+  if ((ntiles - 1) & 1) pv_tile(B1{}, p_prev);
+  else pv_tile(B0{}, p_prev);
 
   // epilogue: lane (query r, half h) holds features 32b + 16h + 0..15 of block b
-  const float l_tot = l_run + swap_halves(l_run);
+  const float l_tot = add_halves(l_run);
   const float inv = 1.0f / l_tot;
   if (qrow >= N) return;
 #pragma unroll
@@ -298,31 +411,41 @@ __global__ __launch_bounds__(256, 2) void anchor_bf16(const uint16_t* __restrict
 
 template <int D>
 hipError_t launch_d(const hla_dims& d, const void* q, const void* k, const void* v, const void* g,
-                    void* out, int accumulate, float scale, hipStream_t stream) {
+                    void* out, int accumulate, float scale, void* ws, hipStream_t stream) {
   const int BH = int(d.B * d.H), N = int(d.N);
+  const int n_pad = (N + kBC - 1) / kBC * kBC;
   const int nqb = (N + kBR - 1) / kBR;
   const int total = BH * nqb;
   const float c = scale * kLog2e;
+  uint16_t* vt = reinterpret_cast<uint16_t*>(ws);
+  hipLaunchKernelGGL(anchor_pack_vt<D>, dim3(n_pad / kBC, BH), dim3(256), 0, stream,
+                     reinterpret_cast<const uint16_t*>(v), vt, N, n_pad);
   if (d.out_dtype == HLA_F32)
     hipLaunchKernelGGL((anchor_bf16<D, true>), dim3(total), dim3(256), 0, stream,
                        reinterpret_cast<const uint16_t*>(q), reinterpret_cast<const uint16_t*>(k),
                        reinterpret_cast<const uint16_t*>(v), reinterpret_cast<const uint16_t*>(g),
-                       out, N, nqb, total, c, accumulate);
+                       vt, out, N, n_pad, nqb, total, c, accumulate);
   else
     hipLaunchKernelGGL((anchor_bf16<D, false>), dim3(total), dim3(256), 0, stream,
                        reinterpret_cast<const uint16_t*>(q), reinterpret_cast<const uint16_t*>(k),
                        reinterpret_cast<const uint16_t*>(v), reinterpret_cast<const uint16_t*>(g),
-                       out, N, nqb, total, c, accumulate);
+                       vt, out, N, n_pad, nqb, total, c, accumulate);
   return hipGetLastError();
 }
 
 }  // namespace
 
+size_t anchor_workspace_bytes(const hla_dims& d) {
+  if (d.in_dtype != HLA_BF16) return 0;
+  const size_t n_pad = size_t((d.N + kBC - 1) / kBC * kBC);
+  return align_up(size_t(d.B * d.H) * size_t(d.D) * n_pad * 2, 256);
+}
+
 hipError_t launch_anchor_bf16(const hla_dims& d, const void* q, const void* k, const void* v,
-                              const void* g, void* out, int accumulate, float scale,
+                              const void* g, void* out, int accumulate, float scale, void* ws,
                               hipStream_t stream) {
-  if (d.D == 128) return launch_d<128>(d, q, k, v, g, out, accumulate, scale, stream);
-  return launch_d<64>(d, q, k, v, g, out, accumulate, scale, stream);
+  if (d.D == 128) return launch_d<128>(d, q, k, v, g, out, accumulate, scale, ws, stream);
+  return launch_d<64>(d, q, k, v, g, out, accumulate, scale, ws, stream);
 }
 
 }  // namespace hla

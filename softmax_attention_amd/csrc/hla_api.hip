@@ -131,6 +131,11 @@ size_t hla_linear_workspace_bytes(const hla_dims* d) {
   return linear_plan(*d).total;
 }
 
+size_t hla_softmax_anchor_workspace_bytes(const hla_dims* d) {
+  if (check_dims(d) != HLA_OK || empty(d)) return 0;
+  return anchor_workspace_bytes(*d);
+}
+
 hla_status hla_linear_fwd(const hla_dims* d, const void* q, const void* k, const void* v,
                           const void* g, void* out, int accumulate, float eps, void* workspace,
                           size_t workspace_bytes, void* stream) {
@@ -152,17 +157,23 @@ hla_status hla_linear_fwd(const hla_dims* d, const void* q, const void* k, const
 
 hla_status hla_softmax_anchor_fwd(const hla_dims* d, const void* q, const void* k, const void* v,
                                   const void* g, void* out, int accumulate, float scale,
-                                  void* stream) {
+                                  void* workspace, size_t workspace_bytes, void* stream) {
   hla_status st = check_dims(d);
   if (st != HLA_OK) return st;
   if (!isfinite(scale) || scale <= 0.f || (accumulate != 0 && accumulate != 1))
     return HLA_ERR_BAD_ARG;
   if (empty(d)) return HLA_OK;
   if ((st = check_tensors(q, k, v, g, out)) != HLA_OK) return st;
+  const size_t need = anchor_workspace_bytes(*d);
+  if (need > 0) {
+    if (!workspace) return HLA_ERR_NULL_PTR;
+    if (!aligned16(workspace)) return HLA_ERR_ALIGN;
+    if (workspace_bytes < need) return HLA_ERR_WORKSPACE;
+  }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   clear_pending_error();
   if (d->in_dtype == HLA_BF16)
-    return from_hip(launch_anchor_bf16(*d, q, k, v, g, out, accumulate, scale, s));
+    return from_hip(launch_anchor_bf16(*d, q, k, v, g, out, accumulate, scale, workspace, s));
   return from_hip(launch_anchor_f32(*d, q, k, v, g, out, accumulate, scale, s));
 }
 
@@ -176,20 +187,26 @@ hla_status hla_hybrid_stack_fwd(const hla_dims* d, int n_layers, const int32_t* 
   if (n_layers <= 0) return HLA_ERR_BAD_ARG;
   if (!kinds || !q || !k || !v || !g) return HLA_ERR_NULL_PTR;
   if (!isfinite(eps) || eps < 0.f || !isfinite(scale) || scale <= 0.f) return HLA_ERR_BAD_ARG;
-  bool any_linear = false;
+  bool any_linear = false, any_softmax = false;
   for (int l = 0; l < n_layers; ++l) {
     if (kinds[l] != HLA_LAYER_LINEAR && kinds[l] != HLA_LAYER_SOFTMAX) return HLA_ERR_BAD_ARG;
     any_linear |= kinds[l] == HLA_LAYER_LINEAR;
+    any_softmax |= kinds[l] == HLA_LAYER_SOFTMAX;
   }
   if (empty(d)) return HLA_OK;
   for (int l = 0; l < n_layers; ++l)
     if ((st = check_tensors(q[l], k[l], v[l], g[l], x)) != HLA_OK) return st;
   LinearPlan plan;
+  size_t need = 0;
   if (any_linear) {
     plan = linear_plan(*d);
+    need = plan.total;
+  }
+  if (any_softmax) need = need > anchor_workspace_bytes(*d) ? need : anchor_workspace_bytes(*d);
+  if (need > 0) {
     if (!workspace) return HLA_ERR_NULL_PTR;
     if (!aligned16(workspace)) return HLA_ERR_ALIGN;
-    if (workspace_bytes < plan.total) return HLA_ERR_WORKSPACE;
+    if (workspace_bytes < need) return HLA_ERR_WORKSPACE;
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool bf = d->in_dtype == HLA_BF16;
@@ -200,7 +217,7 @@ hla_status hla_hybrid_stack_fwd(const hla_dims* d, int n_layers, const int32_t* 
       e = bf ? launch_linear_bf16(*d, q[l], k[l], v[l], g[l], x, 1, eps, workspace, plan, s)
              : launch_linear_f32(*d, q[l], k[l], v[l], g[l], x, 1, eps, workspace, plan, s);
     else
-      e = bf ? launch_anchor_bf16(*d, q[l], k[l], v[l], g[l], x, 1, scale, s)
+      e = bf ? launch_anchor_bf16(*d, q[l], k[l], v[l], g[l], x, 1, scale, workspace, s)
              : launch_anchor_f32(*d, q[l], k[l], v[l], g[l], x, 1, scale, s);
     if (e != hipSuccess) return HLA_ERR_HIP;
   }

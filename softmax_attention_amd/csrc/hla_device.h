@@ -61,9 +61,17 @@ __device__ __forceinline__ float sigmoid(float x) {
   return __builtin_amdgcn_rcpf(1.0f + exp2_fast(-x * kLog2e));
 }
 
-// Value of lane (lane ^ 32): the other half of a wave64.
-__device__ __forceinline__ float swap_halves(float x) {
-  return __shfl_xor(x, 32, 64);
+// Combine x with the value of lane (lane ^ 32), the other half of the wave64,
+// through v_permlane32_swap (no LDS round trip): the swap leaves the two
+// halves' values in its two results, in an order that depends on the lane, so
+// only symmetric combinations are offered.
+__device__ __forceinline__ float max_halves(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+__device__ __forceinline__ float add_halves(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
 // Raw buffer access: a 32-bit byte offset from a per-tensor base; reads past

@@ -119,20 +119,27 @@ __global__ __launch_bounds__(256) void linear_state_bf16(const uint16_t* __restr
     }
   }
 
-  // partial S: C-tile element (q*4 + e) of lane (col r, half h) is row q*8 + 4h + e
+  // partial S, stored in the output pass's fragment order (fp32): element
+  // (row, col) goes to fragment (jb', t) = (2(col>>5) + ((col>>2)&1), row>>5),
+  // lane (g', i') = ((row>>3)&3, 4((col>>3)&3) + (col&3)), slot e' = row&7, so
+  // the reduce reads and writes whole fragments contiguously. C-tile element
+  // (q*4 + e) of lane (col r, half h) is row q*8 + 4h + e: 4 consecutive slots.
   float* P = part + ((size_t)bh * C + c) * (size_t)(D * D + D);
+  constexpr int NT = D / 32;
 #pragma unroll
   for (int x = 0; x < RB; ++x)
 #pragma unroll
-    for (int y = 0; y < RB; ++y)
+    for (int y = 0; y < RB; ++y) {
+      const int t = ib0 + x;
+      const int jbp = 2 * (jb0 + y) + ((r >> 2) & 1);
+      const int ip = 4 * ((r >> 3) & 3) + (r & 3);
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = (ib0 + x) * 32 + q * 8 + 4 * h + e;
-          const int col = (jb0 + y) * 32 + r;
-          P[row * D + col] = acc[x][y][q * 4 + e];
-        }
+      for (int q = 0; q < 4; ++q) {
+        const int idx = ((jbp * NT + t) * 64 + q * 16 + ip) * 8 + 4 * h;
+        *reinterpret_cast<f32x4*>(&P[idx]) =
+            (f32x4){acc[x][y][q * 4], acc[x][y][q * 4 + 1], acc[x][y][q * 4 + 2], acc[x][y][q * 4 + 3]};
+      }
+    }
 
   // partial z: thread tid always loaded feature chunk (tid % CH); sum the
   // 256/CH threads of each chunk in a fixed order
@@ -155,46 +162,62 @@ __global__ __launch_bounds__(256) void linear_state_bf16(const uint16_t* __restr
 // Output pass MFMA (16x16x32): A rows i = lane & 15, k = 8*(lane>>4) + e.
 // Fragment (jb, t) of the numerator holds A[i][k] = S[32t + k][f(jb, i)] with
 // f(jb, i) = 32*(jb>>1) + 8*(i>>2) + 4*(jb&1) + (i&3), so that each output lane
-// ends with 8 consecutive features. Fragment (NJ, t) of the denominator holds
-// z_hi[32t + k] in rows 0..7 and z_lo[32t + k] in rows 8..15.
+// ends with 8 consecutive features; the state pass already stored its partials
+// in this order. Fragment (NJ, t) of the denominator holds z_hi[32t + k] in
+// rows 0..7 and z_lo[32t + k] in rows 8..15. Chunks are summed in order
+// c = 0, 1, ..., C-1 (four independent loads in flight per step).
 template <int D>
 __global__ __launch_bounds__(256) void linear_reduce_bf16(const float* __restrict__ part,
                                                           uint32_t* __restrict__ state, int C) {
   constexpr int NT = D / 32, NJ = D / 16, NF = (NJ + 1) * NT;
-  const int jb = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
-  if (tid >= NT * 64) return;
-  const int t = tid >> 6, l = tid & 63, i = l & 15, g = l >> 4;
+  constexpr int NUM_WG = D * D / 8 / 256;  // workgroups for the numerator fragments
+  const int bh = blockIdx.y, tid = threadIdx.x;
   const size_t stride = (size_t)D * D + D;
   const float* P = part + (size_t)bh * C * stride;
-  uint32_t w[4];
-  if (jb < NJ) {
-    const int f = 32 * (jb >> 1) + 8 * (i >> 2) + 4 * (jb & 1) + (i & 3);
-    float v[8];
+  uint32_t* St = state + (size_t)bh * NF * 256;
+  auto sum8 = [&](size_t off, float* v) {
+    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+    int c = 0;
+    for (; c + 4 <= C; c += 4) {
+      f32x4 x[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int row = 32 * t + 8 * g + e;
-      float s = 0.f;
-      for (int c = 0; c < C; ++c) s += P[c * stride + row * D + f];
-      v[e] = s;
+      for (int u = 0; u < 4; ++u) {
+        x[2 * u] = *reinterpret_cast<const f32x4*>(P + (c + u) * stride + off);
+        x[2 * u + 1] = *reinterpret_cast<const f32x4*>(P + (c + u) * stride + off + 4);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        a0 += x[2 * u];
+        a1 += x[2 * u + 1];
+      }
+    }
+    for (; c < C; ++c) {
+      a0 += *reinterpret_cast<const f32x4*>(P + c * stride + off);
+      a1 += *reinterpret_cast<const f32x4*>(P + c * stride + off + 4);
     }
 #pragma unroll
-    for (int p = 0; p < 4; ++p) w[p] = pack_bf16(v[2 * p], v[2 * p + 1]);
-  } else {
-    float v[8];
+    for (int e = 0; e < 4; ++e) {
+      v[e] = a0[e];
+      v[4 + e] = a1[e];
+    }
+  };
+  float v[8];
+  if (blockIdx.x < NUM_WG) {
+    const int x = blockIdx.x * 256 + tid;  // (fragment, lane) pair; 8 slots each
+    sum8((size_t)x * 8, v);
+    *reinterpret_cast<u32x4*>(St + (size_t)x * 4) =
+        (u32x4){pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]), pack_bf16(v[4], v[5]), pack_bf16(v[6], v[7])};
+  } else if (tid < NT * 64) {
+    const int t = tid >> 6, l = tid & 63, i = l & 15, g = l >> 4;
+    sum8((size_t)D * D + 32 * t + 8 * g, v);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int d = 32 * t + 8 * g + e;
-      float s = 0.f;
-      for (int c = 0; c < C; ++c) s += P[c * stride + D * D + d];
-      const float hi = bf16_to_f32(f32_to_bf16(s));
-      v[e] = (i < 8) ? hi : (s - hi);
+      const float hi = bf16_to_f32(f32_to_bf16(v[e]));
+      v[e] = (i < 8) ? hi : (v[e] - hi);
     }
-#pragma unroll
-    for (int p = 0; p < 4; ++p) w[p] = pack_bf16(v[2 * p], v[2 * p + 1]);
+    *reinterpret_cast<u32x4*>(St + ((size_t)(NJ * NT + t) * 64 + l) * 4) =
+        (u32x4){pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]), pack_bf16(v[4], v[5]), pack_bf16(v[6], v[7])};
   }
-  const int fi = (jb < NJ) ? jb * NT + t : NJ * NT + t;
-  uint32_t* dst = state + ((size_t)bh * NF + fi) * 256 + l * 4;
-  *reinterpret_cast<u32x4*>(dst) = (u32x4){w[0], w[1], w[2], w[3]};
 }
 
 // ---------------------------------------------------------------------------
@@ -266,7 +289,7 @@ __global__ __launch_bounds__(256, 2) void linear_out_bf16(const uint16_t* __rest
       for (int j = 0; j < NJ; ++j) acc[j] = mfma16x16x32(fr[(j * NT + t) * 64 + fo], b, acc[j]);
       accd = mfma16x16x32(fr[(NJ * NT + t) * 64 + fo], b, accd);
     }
-    const float den = accd[0] + swap_halves(accd[0]) + eps;
+    const float den = add_halves(accd[0]) + eps;
     const float rden = 1.0f / den;
 
     const int tok = grp * 16 + n;
@@ -331,8 +354,8 @@ hipError_t launch_d(const hla_dims& d, const void* q, const void* k, const void*
   hipLaunchKernelGGL(linear_state_bf16<D>, dim3(plan.C, BH), dim3(256), 0, stream,
                      reinterpret_cast<const uint16_t*>(k), reinterpret_cast<const uint16_t*>(v),
                      part, N, plan.T, plan.C);
-  hipLaunchKernelGGL(linear_reduce_bf16<D>, dim3(D / 16 + 1, BH), dim3(256), 0, stream, part,
-                     state, plan.C);
+  hipLaunchKernelGGL(linear_reduce_bf16<D>, dim3(D * D / 8 / 256 + 1, BH), dim3(256), 0, stream,
+                     part, state, plan.C);
   if (d.out_dtype == HLA_F32)
     hipLaunchKernelGGL((linear_out_bf16<D, true>), dim3(plan.P, BH), dim3(256), 0, stream,
                        reinterpret_cast<const uint16_t*>(q), reinterpret_cast<const uint16_t*>(g),

@@ -38,9 +38,9 @@ def lin(d, q=FAKE, k=FAKE, v=FAKE, g=FAKE, out=FAKE, acc=0, eps=1e-6, ws=FAKE, w
                                   eps, ws, wsb, None)
 
 
-def sm(d, q=FAKE, k=FAKE, v=FAKE, g=FAKE, out=FAKE, acc=0, scale=0.1):
+def sm(d, q=FAKE, k=FAKE, v=FAKE, g=FAKE, out=FAKE, acc=0, scale=0.1, ws=FAKE, wsb=1 << 40):
     return hla.lib.hla_softmax_anchor_fwd(ctypes.byref(d) if d is not None else None, q, k, v, g,
-                                          out, acc, scale, None)
+                                          out, acc, scale, ws, wsb, None)
 
 
 def stack(d, n=2, kinds=(0, 1), ptrs=None, x=FAKE, eps=1e-6, scale=0.1, ws=FAKE, wsb=1 << 40):
@@ -67,7 +67,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert hla.hla_abi_version() == 1
+    assert hla.hla_abi_version() == 2
     for code, name in hla.STATUS.items():
         assert hla.hla_status_str(code) == name
     assert hla.hla_status_str(99) == "HLA_UNKNOWN"
@@ -129,6 +129,23 @@ def test_softmax_argument_errors():
     for s in (0.0, -0.1, float("nan"), float("inf")):
         assert sm(d, scale=s) == BADARG
     assert sm(d, acc=3) == BADARG
+    assert sm(d, ws=None) == NULLP
+    assert sm(d, ws=ODD) == ALIGN
+    need = hla.hla_softmax_anchor_workspace_bytes(d)
+    assert sm(d, wsb=need - 1) == WS
+    # the fp32 path needs no workspace: validation then rejects nothing about it,
+    # so only check the size query here (a valid fp32 call would launch)
+    assert hla.hla_softmax_anchor_workspace_bytes(dims(i=F32, o=F32, D=32)) == 0
+
+
+def test_softmax_workspace_size():
+    # repacked V^T: B*H*D*ceil(N/64)*64 bf16, rounded up to 256 bytes
+    for (B, H, N, D) in [(2, 16, 19320, 128), (1, 2, 1, 64), (1, 1, 64, 128), (1, 1, 65, 128)]:
+        n_pad = -(-N // 64) * 64
+        want = -(-(B * H * D * n_pad * 2) // 256) * 256
+        assert hla.hla_softmax_anchor_workspace_bytes(dims(B, H, N, D)) == want
+    assert hla.hla_softmax_anchor_workspace_bytes(dims(N=0)) == 0
+    assert hla.lib.hla_softmax_anchor_workspace_bytes(None) == 0
 
 
 def test_stack_argument_errors():
@@ -146,7 +163,9 @@ def test_stack_argument_errors():
     assert stack(d, x=None) == NULLP
     assert stack(d, x=ODD) == ALIGN
     assert stack(d, ws=None) == NULLP                           # has a linear layer
-    assert stack(d, wsb=hla.hla_linear_workspace_bytes(d) - 16) == WS
+    need = max(hla.hla_linear_workspace_bytes(d), hla.hla_softmax_anchor_workspace_bytes(d))
+    assert stack(d, wsb=need - 16) == WS
+    assert stack(d, kinds=(1, 1), wsb=hla.hla_softmax_anchor_workspace_bytes(d) - 16) == WS
     assert stack(dims(D=40, o=F32)) == UNSUP
     assert stack(dims(N=-1, o=F32)) == SHAPE
 
@@ -155,7 +174,7 @@ def test_empty_tensors_are_a_no_op():
     # B*H*N == 0: valid, nothing to do, pointers may be NULL
     for d in (dims(N=0), dims(B=0), dims(H=0, i=F32, o=F32, D=32)):
         assert lin(d, q=None, k=None, v=None, g=None, out=None, ws=None, wsb=0) == OK
-        assert sm(d, q=None, k=None, v=None, g=None, out=None) == OK
+        assert sm(d, q=None, k=None, v=None, g=None, out=None, ws=None, wsb=0) == OK
         assert stack(d, ptrs=[None, None], x=None, ws=None, wsb=0) == OK
     # but the other arguments are still checked
     assert lin(dims(N=0), eps=-1.0) == BADARG

@@ -167,12 +167,15 @@ def main():
         hla.hla_softmax_anchor_fwd(q, k, v, g, out=outs[1], scale=w.scale, workspace=ws_a)
 
     if args.profile:
+        # args.warmup untimed launches first, then args.iters; a trace summary
+        # drops the first args.warmup launches of each kernel
         fn = {"anchor": [anchor], "linear": [linear], "step": [linear, anchor]}[args.profile]
-        for i in range(args.iters):
+        for i in range(args.warmup + args.iters):
             for f in fn:
                 f(i)
         torch.cuda.synchronize()
-        print(json.dumps({"profile": args.profile, "workload": w.name, "iters": args.iters}))
+        print(json.dumps({"profile": args.profile, "workload": w.name, "warmup": args.warmup,
+                          "iters": args.iters}))
         return
 
     for i in range(args.warmup):

@@ -250,14 +250,17 @@ __global__ __launch_bounds__(256, 2) void anchor_bf16(const uint16_t* __restrict
           if (key >= N) s[kb][x] = -INFINITY;
         }
     }
-    // row max: a tree (short dependency chains), then the partner half-wave
-    float m16[16];
+    // row max: two chains of 3-input maxima, then the partner half-wave.
+    // maximum (NaN-propagating) needs no canonicalizing of the MFMA results,
+    // which fmaxf would add for every score.
+    float m2[2];
 #pragma unroll
-    for (int x = 0; x < 16; ++x) m16[x] = fmaxf(s[0][x], s[1][x]);
+    for (int kb = 0; kb < 2; ++kb) {
+      m2[kb] = s[kb][0];
 #pragma unroll
-    for (int w = 8; w >= 1; w >>= 1)
-#pragma unroll
-      for (int x = 0; x < w; ++x) m16[x] = fmaxf(m16[x], m16[x + w]);
+      for (int x = 1; x < 16; ++x) m2[kb] = __builtin_elementwise_maximum(m2[kb], s[kb][x]);
+    }
+    float m16[1] = {__builtin_elementwise_maximum(m2[0], m2[1])};
     const float mt = max_halves(m16[0]) * c;
     const bool need = mt > m_run + kTau;
     const float m_new = need ? mt : m_run;

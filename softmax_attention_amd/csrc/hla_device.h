@@ -67,7 +67,7 @@ __device__ __forceinline__ float sigmoid(float x) {
 // only symmetric combinations are offered.
 __device__ __forceinline__ float max_halves(float x) {
   const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+  return __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
 }
 __device__ __forceinline__ float add_halves(float x) {
   const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -39,11 +39,19 @@ KERNEL_SOURCES = {
 }
 
 
+def code_only(src: str) -> str:
+    """C++ source with comments and blank runs removed: edits to comments do not
+    change the kernel, so they must not invalidate its recorded counters."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    return "\n".join(" ".join(line.split()) for line in src.splitlines() if line.strip())
+
+
 def kernel_hash(which: str) -> str:
     h = hashlib.sha256()
     for p in KERNEL_SOURCES[which]:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p)) as f:
+            h.update(code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -17,10 +17,12 @@
 //                    result exact up to rounding.
 //   O^T += V^T P^T   P^T stays in registers (the MFMA result layout is reused as
 //                    the next B operand by permuting the key order inside each
-//                    k-step); V stays row-major in LDS and the V^T operand comes
-//                    from two LDS transpose reads per MFMA.
-// K and V tiles arrive through buffer loads, which return zeros past the end of
-// the head, so the last partial tile needs no predicated loads.
+//                    k-step). V is repacked once per call into V^T rows (a
+//                    workspace, zero keys past N) in the key order P^T uses,
+//                    so each V^T operand is one 16-byte LDS read.
+// K and V^T tiles go from HBM straight into LDS through buffer loads, which
+// return zeros past the end of the head, so the last partial tile needs no
+// predicated loads; only its scores past N are masked.
 // The epilogue divides by the row sum, applies the sigmoid gate and stores O
 // (bf16) or adds it into an fp32 residual stream.
 #include <type_traits>

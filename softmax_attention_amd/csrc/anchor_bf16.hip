@@ -5,8 +5,10 @@
 // between gated linear layers (SANA-Video 2.0 abstract, thelatestinai.com
 // listing; lode.cx article, "The Core Innovation" and "How It Works").
 //
-// Flash-style single pass: a workgroup owns 128 query rows (4 waves x 32) of
-// one (b, h) and streams all keys through LDS in tiles of 64, double-buffered.
+// Flash-style single pass: a workgroup owns 256 query rows (8 waves x 32, two
+// waves per SIMD) of one (b, h) and streams all keys through LDS in tiles of
+// 64, double-buffered; the eight waves share each tile, so K and V cross from
+// L2 into LDS once per 256 queries.
 // Per tile and wave:
 //   S^T = K Q^T      32x32x16 bf16 MFMA, K from LDS, Q^T held in registers; the
 //                    transposed product puts one query per lane (and its
@@ -33,7 +35,9 @@
 namespace hla {
 namespace {
 
-constexpr int kBR = 128;  // query rows per workgroup
+constexpr int kWaves = 8;               // waves per workgroup, 32 query rows each
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBR = 32 * kWaves;        // query rows per workgroup
 constexpr int kBC = 64;   // keys per LDS tile
 constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
 
@@ -105,7 +109,7 @@ __global__ __launch_bounds__(256) void anchor_pack_vt(const uint16_t* __restrict
 }
 
 template <int D, bool OUT_F32>
-__global__ __launch_bounds__(256, 2) void anchor_bf16(const uint16_t* __restrict__ Q,
+__global__ __launch_bounds__(kThreads, 1) void anchor_bf16(const uint16_t* __restrict__ Q,
                                                       const uint16_t* __restrict__ K,
                                                       const uint16_t* __restrict__ V,
                                                       const uint16_t* __restrict__ G,
@@ -116,7 +120,7 @@ __global__ __launch_bounds__(256, 2) void anchor_bf16(const uint16_t* __restrict
   constexpr int NK = D / 16;              // k-steps of S^T
   constexpr int ND = D / 32;              // 32-row blocks of O^T
   constexpr int CH = D / 8;               // 16-byte chunks per row
-  constexpr int LOADS = kBC * CH / 256;   // 16-byte loads per thread per tensor per tile
+  constexpr int LOADS = kBC * CH / kThreads;  // 16-byte loads per thread per tensor per tile
   constexpr uint32_t kTileBytes = kBC * D * 2;
   using Swz = AnchorSwz<D>;
   // Four separate LDS arrays rather than two [2][...] ones: the compiler then
@@ -439,12 +443,12 @@ hipError_t launch_d(const hla_dims& d, const void* q, const void* k, const void*
   hipLaunchKernelGGL(anchor_pack_vt<D>, dim3(n_pad / kBC, BH), dim3(256), 0, stream,
                      reinterpret_cast<const uint16_t*>(v), vt, N, n_pad);
   if (d.out_dtype == HLA_F32)
-    hipLaunchKernelGGL((anchor_bf16<D, true>), dim3(total), dim3(256), 0, stream,
+    hipLaunchKernelGGL((anchor_bf16<D, true>), dim3(total), dim3(kThreads), 0, stream,
                        reinterpret_cast<const uint16_t*>(q), reinterpret_cast<const uint16_t*>(k),
                        reinterpret_cast<const uint16_t*>(v), reinterpret_cast<const uint16_t*>(g),
                        vt, out, N, n_pad, nqb, total, c, accumulate);
   else
-    hipLaunchKernelGGL((anchor_bf16<D, false>), dim3(total), dim3(256), 0, stream,
+    hipLaunchKernelGGL((anchor_bf16<D, false>), dim3(total), dim3(kThreads), 0, stream,
                        reinterpret_cast<const uint16_t*>(q), reinterpret_cast<const uint16_t*>(k),
                        reinterpret_cast<const uint16_t*>(v), reinterpret_cast<const uint16_t*>(g),
                        vt, out, N, n_pad, nqb, total, c, accumulate);

@@ -40,6 +40,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kBR = 32 * kWaves;        // query rows per workgroup
 constexpr int kBC = 64;   // keys per LDS tile
 constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
+constexpr int kMaxPieces = 256;  // most key-range pieces one call splits its last round into
 
 // LDS tiles use XOR swizzles of whole 16-byte chunks instead of padding:
 //   K   (row = key, D/8 chunks): chunk c of row k sits at c ^ (k & 15)
@@ -115,8 +116,9 @@ __global__ __launch_bounds__(kThreads, 1) void anchor_bf16(const uint16_t* __res
                                                       const uint16_t* __restrict__ G,
                                                       const uint16_t* __restrict__ VT,
                                                       void* __restrict__ out, int N, int n_pad,
-                                                      int nqb, int total, float c,
-                                                      int accumulate) {
+                                                      int nqb, int nmain, int split, float c,
+                                                      int accumulate, float* __restrict__ part,
+                                                      float* __restrict__ part_ml) {
   constexpr int NK = D / 16;              // k-steps of S^T
   constexpr int ND = D / 32;              // 32-row blocks of O^T
   constexpr int CH = D / 8;               // 16-byte chunks per row
@@ -139,14 +141,23 @@ __global__ __launch_bounds__(kThreads, 1) void anchor_bf16(const uint16_t* __res
     else return Vs1;
   };
 
-  // Workgroups are dispatched round-robin over the 8 XCDs; renumber them so
-  // each XCD runs a contiguous range of (b, h, query block) and the query
-  // blocks of one head share that XCD's L2 while streaming its K and V.
+  // The first nmain workgroups each own one query block over all keys. They are
+  // dispatched round-robin over the 8 XCDs; renumber them so each XCD runs a
+  // contiguous range of (b, h, query block) and the query blocks of one head
+  // share that XCD's L2 while streaming its K and V. The workgroups after them
+  // (dispatched last) split each remaining query block into `split` key ranges,
+  // so the last round of workgroups is short; they leave unnormalised partial
+  // results in `part` for anchor_combine.
   const int bid = blockIdx.x;
-  const int xcd = bid & 7, local = bid >> 3;
-  const int per = total >> 3, rem = total & 7;
-  const int logical =
-      xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+  int logical, piece = -1;
+  if (bid < nmain) {
+    const int xcd = bid & 7, local = bid >> 3;
+    const int per = nmain >> 3, rem = nmain & 7;
+    logical = xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+  } else {
+    piece = bid - nmain;
+    logical = nmain + piece / split;
+  }
   const int bh = logical / nqb, qb = logical - bh * nqb;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -218,6 +229,9 @@ __global__ __launch_bounds__(kThreads, 1) void anchor_bf16(const uint16_t* __res
   float m_run = -INFINITY, l_run = 0.f;
   const int ntiles = (N + kBC - 1) / kBC;
   const bool ragged = (N % kBC) != 0;
+  // key tiles [t0, t1) of this workgroup
+  const int t0 = piece < 0 ? 0 : (piece % split) * ntiles / split;
+  const int t1 = piece < 0 ? ntiles : (piece % split + 1) * ntiles / split;
 
   // ---- building blocks -----------------------------------------------------
   // S^T of the tile held in K buffer KB (two 32-key blocks)
@@ -339,9 +353,9 @@ __global__ __launch_bounds__(kThreads, 1) void anchor_bf16(const uint16_t* __res
     u32x4 p_cur[4];
     const bool mask = !STEADY && ragged && j == ntiles - 1;
     const float alpha = softmax(s_cur, p_cur, j, mask);
-    if (STEADY || j > 0) pv_tile(Oth{}, p_prev);
+    if (STEADY || j > t0) pv_tile(Oth{}, p_prev);
     f32x16 s_next[2];
-    if (STEADY || j + 1 < ntiles) s_tile(Oth{}, s_next);
+    if (STEADY || j + 1 < t1) s_tile(Oth{}, s_next);
     // and keep P(j) and the row sum from sinking below them: they are used by
     // the next iteration only, so the compiler would otherwise compute them late
     asm volatile("" ::"v"(p_cur[0]), "v"(p_cur[1]), "v"(p_cur[2]), "v"(p_cur[3]), "v"(l_run));
@@ -361,31 +375,52 @@ __global__ __launch_bounds__(kThreads, 1) void anchor_bf16(const uint16_t* __res
   using Steady = std::true_type;
   using Edge = std::false_type;
 
-  // prologue: K(0), K(1) in; S^T of tile 0
-  load_k(0, std::integral_constant<int, 0>{});
-  if (ntiles > 1) load_k(1, std::integral_constant<int, 1>{});
+  // prologue: K(t0), K(t0+1) in; S^T of tile t0
+  const int nt = t1 - t0;
+  load_k(t0, B0{});
+  if (nt > 1) load_k(t0 + 1, B1{});
   wait_all_memory();
   __syncthreads();
   s_tile(B0{}, s_cur);
-  __syncthreads();  // K buffer 0 is free for K(2)
+  __syncthreads();  // K buffer 0 is free for K(t0+2)
 
-  iteration(B0{}, Edge{}, 0);
-  int j = 1;
-  for (; j + 2 <= ntiles - 1; j += 2) {  // tiles 1 .. ntiles-2 are steady
-    iteration(B1{}, Steady{}, j);
-    iteration(B0{}, Steady{}, j + 1);
+  // buffer parity follows the tile's position in the range
+  iteration(B0{}, Edge{}, t0);
+  int jl = 1;
+  for (; jl + 2 <= nt - 1; jl += 2) {  // local tiles 1 .. nt-2 are steady
+    iteration(B1{}, Steady{}, t0 + jl);
+    iteration(B0{}, Steady{}, t0 + jl + 1);
   }
-  if (j <= ntiles - 2) {
-    iteration(B1{}, Steady{}, j);
-    ++j;
+  if (jl <= nt - 2) {
+    iteration(B1{}, Steady{}, t0 + jl);
+    ++jl;
   }
-  if (j == ntiles - 1 && j > 0) {  // the last tile
-    if (j & 1) iteration(B1{}, Edge{}, j);
-    else iteration(B0{}, Edge{}, j);
+  if (jl == nt - 1 && jl > 0) {  // the last tile
+    if (jl & 1) iteration(B1{}, Edge{}, t0 + jl);
+    else iteration(B0{}, Edge{}, t0 + jl);
   }
   // P V of the last tile
-  if ((ntiles - 1) & 1) pv_tile(B1{}, p_prev);
+  if ((nt - 1) & 1) pv_tile(B1{}, p_prev);
   else pv_tile(B0{}, p_prev);
+
+  if (piece >= 0) {
+    // partial result of a key range: unnormalised O, running max and row sum
+    const float l_tot = add_halves(l_run);
+    const int row = wave * 32 + r;
+    float* po = part + ((size_t)piece * kBR + row) * D;
+#pragma unroll
+    for (int b = 0; b < ND; ++b)
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+        *reinterpret_cast<f32x4*>(po + 32 * b + 16 * h + 4 * x) =
+            (f32x4){acc[b][4 * x], acc[b][4 * x + 1], acc[b][4 * x + 2], acc[b][4 * x + 3]};
+    if (h == 0) {
+      float* pml = part_ml + ((size_t)piece * kBR + row) * 2;
+      pml[0] = m_run;
+      pml[1] = l_tot;
+    }
+    return;
+  }
 
   // epilogue: lane (query r, half h) holds features 32b + 16h + 0..15 of block b
   const float l_tot = add_halves(l_run);
@@ -431,27 +466,156 @@ __global__ __launch_bounds__(kThreads, 1) void anchor_bf16(const uint16_t* __res
   }
 }
 
+// ---------------------------------------------------------------------------
+// Merge the key-range pieces of the split query blocks: with per-piece running
+// max m_p (log2 units), row sum l_p and unnormalised O_p, the full row is
+// O = sum_p 2^(m_p - m) O_p / sum_p 2^(m_p - m) l_p, m = max_p m_p; then the
+// gate and the store, as in the main epilogue. One thread per query row.
+// ---------------------------------------------------------------------------
+template <int D, bool OUT_F32>
+__global__ __launch_bounds__(kBR) void anchor_combine(const float* __restrict__ part,
+                                                      const float* __restrict__ part_ml,
+                                                      const uint16_t* __restrict__ G,
+                                                      void* __restrict__ out, int N, int nqb,
+                                                      int nmain, int split, int accumulate) {
+  const int tb = blockIdx.x, row = threadIdx.x;
+  const int logical = nmain + tb;
+  const int bh = logical / nqb, qb = logical - bh * nqb;
+  const int qrow = qb * kBR + row;
+  if (qrow >= N) return;
+  const float* ml = part_ml + ((size_t)tb * split * kBR + row) * 2;  // piece p at + p kBR 2
+  const float* po = part + ((size_t)tb * split * kBR + row) * D;     // piece p at + p kBR D
+  float m = -INFINITY;
+  for (int p = 0; p < split; ++p) m = fmaxf(m, ml[(size_t)p * kBR * 2]);
+  float wsum = 0.f;
+  for (int p = 0; p < split; ++p)
+    wsum = fmaf(exp2_fast(ml[(size_t)p * kBR * 2] - m), ml[(size_t)p * kBR * 2 + 1], wsum);
+  const float inv = 1.0f / wsum;
+  const size_t base = ((size_t)bh * N + qrow) * D;
+  for (int f = 0; f < D; f += 8) {
+    float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < split; ++p) {
+      const float wp = exp2_fast(ml[(size_t)p * kBR * 2] - m);
+      const f32x4 a = *reinterpret_cast<const f32x4*>(po + (size_t)p * kBR * D + f);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(po + (size_t)p * kBR * D + f + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[e] = fmaf(wp, a[e], o[e]);
+        o[4 + e] = fmaf(wp, b[e], o[4 + e]);
+      }
+    }
+    const u32x4 gv = ldg16(G + base + f);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      o[2 * e] = (o[2 * e] * inv) * sigmoid(bf_lo(gv[e]));
+      o[2 * e + 1] = (o[2 * e + 1] * inv) * sigmoid(bf_hi(gv[e]));
+    }
+    if (OUT_F32) {
+      float* dst = reinterpret_cast<float*>(out) + base + f;
+      f32x4 lo = (f32x4){o[0], o[1], o[2], o[3]}, hi = (f32x4){o[4], o[5], o[6], o[7]};
+      if (accumulate) {
+        lo += *reinterpret_cast<const f32x4*>(dst);
+        hi += *reinterpret_cast<const f32x4*>(dst + 4);
+      }
+      *reinterpret_cast<f32x4*>(dst) = lo;
+      *reinterpret_cast<f32x4*>(dst + 4) = hi;
+    } else {
+      uint16_t* dst = reinterpret_cast<uint16_t*>(out) + base + f;
+      if (accumulate) {
+        const u32x4 prev = ldg16(dst);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          o[2 * e] += bf_lo(prev[e]);
+          o[2 * e + 1] += bf_hi(prev[e]);
+        }
+      }
+      stg16(dst, (u32x4){pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]), pack_bf16(o[4], o[5]),
+                         pack_bf16(o[6], o[7])});
+    }
+  }
+}
+
+// Compute units of the current device (one anchor workgroup fits per CU).
+int device_cus() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+struct AnchorLayout {
+  size_t vt_bytes, part_off, ml_off, total;
+  int pieces_cap;
+};
+AnchorLayout anchor_layout(const hla_dims& d) {
+  AnchorLayout L;
+  const int64_t BH = d.B * d.H, N = d.N, D = d.D;
+  const int64_t n_pad = (N + kBC - 1) / kBC * kBC;
+  const int64_t nqb = (N + kBR - 1) / kBR, ntiles = n_pad / kBC;
+  const int64_t cap = BH * nqb * ntiles;
+  L.pieces_cap = int(cap < kMaxPieces ? cap : kMaxPieces);
+  L.vt_bytes = align_up(size_t(BH * D * n_pad * 2), 256);
+  L.part_off = L.vt_bytes;
+  L.ml_off = L.part_off + align_up(size_t(L.pieces_cap) * kBR * D * 4, 256);
+  L.total = L.ml_off + align_up(size_t(L.pieces_cap) * kBR * 2 * 4, 256);
+  return L;
+}
+
 template <int D>
 hipError_t launch_d(const hla_dims& d, const void* q, const void* k, const void* v, const void* g,
                     void* out, int accumulate, float scale, void* ws, hipStream_t stream) {
   const int BH = int(d.B * d.H), N = int(d.N);
   const int n_pad = (N + kBC - 1) / kBC * kBC;
+  const int ntiles = n_pad / kBC;
   const int nqb = (N + kBR - 1) / kBR;
   const int total = BH * nqb;
   const float c = scale * kLog2e;
-  uint16_t* vt = reinterpret_cast<uint16_t*>(ws);
+  const AnchorLayout L = anchor_layout(d);
+  char* w = reinterpret_cast<char*>(ws);
+  uint16_t* vt = reinterpret_cast<uint16_t*>(w);
+  float* part = reinterpret_cast<float*>(w + L.part_off);
+  float* part_ml = reinterpret_cast<float*>(w + L.ml_off);
+  // Workgroups run one round per CU at a time. The query blocks of an
+  // incomplete last round are split along the keys so that round takes a
+  // fraction of a full one.
+  const int slots = device_cus();
+  int tail = total % slots, split = 1;
+  if (tail > 0) {
+    split = slots / tail;
+    if (split > ntiles) split = ntiles;
+    if (split > L.pieces_cap / tail) split = L.pieces_cap / tail;
+  }
+  if (split < 2) {
+    tail = 0;
+    split = 1;
+  }
+  const int nmain = total - tail;
+  const int grid = nmain + tail * split;
   hipLaunchKernelGGL(anchor_pack_vt<D>, dim3(n_pad / kBC, BH), dim3(256), 0, stream,
                      reinterpret_cast<const uint16_t*>(v), vt, N, n_pad);
-  if (d.out_dtype == HLA_F32)
-    hipLaunchKernelGGL((anchor_bf16<D, true>), dim3(total), dim3(kThreads), 0, stream,
-                       reinterpret_cast<const uint16_t*>(q), reinterpret_cast<const uint16_t*>(k),
-                       reinterpret_cast<const uint16_t*>(v), reinterpret_cast<const uint16_t*>(g),
-                       vt, out, N, n_pad, nqb, total, c, accumulate);
-  else
-    hipLaunchKernelGGL((anchor_bf16<D, false>), dim3(total), dim3(kThreads), 0, stream,
-                       reinterpret_cast<const uint16_t*>(q), reinterpret_cast<const uint16_t*>(k),
-                       reinterpret_cast<const uint16_t*>(v), reinterpret_cast<const uint16_t*>(g),
-                       vt, out, N, n_pad, nqb, total, c, accumulate);
+  const uint16_t* Qp = reinterpret_cast<const uint16_t*>(q);
+  const uint16_t* Kp = reinterpret_cast<const uint16_t*>(k);
+  const uint16_t* Vp = reinterpret_cast<const uint16_t*>(v);
+  const uint16_t* Gp = reinterpret_cast<const uint16_t*>(g);
+  if (d.out_dtype == HLA_F32) {
+    hipLaunchKernelGGL((anchor_bf16<D, true>), dim3(grid), dim3(kThreads), 0, stream, Qp, Kp, Vp,
+                       Gp, vt, out, N, n_pad, nqb, nmain, split, c, accumulate, part, part_ml);
+    if (tail > 0)
+      hipLaunchKernelGGL((anchor_combine<D, true>), dim3(tail), dim3(kBR), 0, stream, part,
+                         part_ml, Gp, out, N, nqb, nmain, split, accumulate);
+  } else {
+    hipLaunchKernelGGL((anchor_bf16<D, false>), dim3(grid), dim3(kThreads), 0, stream, Qp, Kp, Vp,
+                       Gp, vt, out, N, n_pad, nqb, nmain, split, c, accumulate, part, part_ml);
+    if (tail > 0)
+      hipLaunchKernelGGL((anchor_combine<D, false>), dim3(tail), dim3(kBR), 0, stream, part,
+                         part_ml, Gp, out, N, nqb, nmain, split, accumulate);
+  }
   return hipGetLastError();
 }
 
@@ -459,8 +623,7 @@ hipError_t launch_d(const hla_dims& d, const void* q, const void* k, const void*
 
 size_t anchor_workspace_bytes(const hla_dims& d) {
   if (d.in_dtype != HLA_BF16) return 0;
-  const size_t n_pad = size_t((d.N + kBC - 1) / kBC * kBC);
-  return align_up(size_t(d.B * d.H) * size_t(d.D) * n_pad * 2, 256);
+  return anchor_layout(d).total;
 }
 
 hipError_t launch_anchor_bf16(const hla_dims& d, const void* q, const void* k, const void* v,

@@ -470,68 +470,71 @@ __global__ __launch_bounds__(kThreads, 1) void anchor_bf16(const uint16_t* __res
 // Merge the key-range pieces of the split query blocks: with per-piece running
 // max m_p (log2 units), row sum l_p and unnormalised O_p, the full row is
 // O = sum_p 2^(m_p - m) O_p / sum_p 2^(m_p - m) l_p, m = max_p m_p; then the
-// gate and the store, as in the main epilogue. One thread per query row.
+// gate and the store, as in the main epilogue. Each thread takes 8 features of
+// one query row; 16 rows per workgroup, kBR / 16 workgroups per split block.
 // ---------------------------------------------------------------------------
 template <int D, bool OUT_F32>
-__global__ __launch_bounds__(kBR) void anchor_combine(const float* __restrict__ part,
+__global__ __launch_bounds__(256) void anchor_combine(const float* __restrict__ part,
                                                       const float* __restrict__ part_ml,
                                                       const uint16_t* __restrict__ G,
                                                       void* __restrict__ out, int N, int nqb,
                                                       int nmain, int split, int accumulate) {
-  const int tb = blockIdx.x, row = threadIdx.x;
+  constexpr int TPR = D / 8;                 // threads per row
+  constexpr int RPB = 256 / TPR;             // rows per workgroup
+  constexpr int WPB = kBR / RPB;             // workgroups per split block
+  const int tb = blockIdx.x / WPB;
+  const int row = (blockIdx.x % WPB) * RPB + threadIdx.x / TPR;
+  const int f = (threadIdx.x % TPR) * 8;
   const int logical = nmain + tb;
   const int bh = logical / nqb, qb = logical - bh * nqb;
   const int qrow = qb * kBR + row;
   if (qrow >= N) return;
   const float* ml = part_ml + ((size_t)tb * split * kBR + row) * 2;  // piece p at + p kBR 2
-  const float* po = part + ((size_t)tb * split * kBR + row) * D;     // piece p at + p kBR D
+  const float* po = part + ((size_t)tb * split * kBR + row) * D + f;  // piece p at + p kBR D
   float m = -INFINITY;
   for (int p = 0; p < split; ++p) m = fmaxf(m, ml[(size_t)p * kBR * 2]);
   float wsum = 0.f;
-  for (int p = 0; p < split; ++p)
-    wsum = fmaf(exp2_fast(ml[(size_t)p * kBR * 2] - m), ml[(size_t)p * kBR * 2 + 1], wsum);
-  const float inv = 1.0f / wsum;
-  const size_t base = ((size_t)bh * N + qrow) * D;
-  for (int f = 0; f < D; f += 8) {
-    float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int p = 0; p < split; ++p) {
-      const float wp = exp2_fast(ml[(size_t)p * kBR * 2] - m);
-      const f32x4 a = *reinterpret_cast<const f32x4*>(po + (size_t)p * kBR * D + f);
-      const f32x4 b = *reinterpret_cast<const f32x4*>(po + (size_t)p * kBR * D + f + 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        o[e] = fmaf(wp, a[e], o[e]);
-        o[4 + e] = fmaf(wp, b[e], o[4 + e]);
-      }
-    }
-    const u32x4 gv = ldg16(G + base + f);
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int p = 0; p < split; ++p) {
+    const float wp = exp2_fast(ml[(size_t)p * kBR * 2] - m);
+    wsum = fmaf(wp, ml[(size_t)p * kBR * 2 + 1], wsum);
+    const f32x4 a = *reinterpret_cast<const f32x4*>(po + (size_t)p * kBR * D);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(po + (size_t)p * kBR * D + 4);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      o[2 * e] = (o[2 * e] * inv) * sigmoid(bf_lo(gv[e]));
-      o[2 * e + 1] = (o[2 * e + 1] * inv) * sigmoid(bf_hi(gv[e]));
+      o[e] = fmaf(wp, a[e], o[e]);
+      o[4 + e] = fmaf(wp, b[e], o[4 + e]);
     }
-    if (OUT_F32) {
-      float* dst = reinterpret_cast<float*>(out) + base + f;
-      f32x4 lo = (f32x4){o[0], o[1], o[2], o[3]}, hi = (f32x4){o[4], o[5], o[6], o[7]};
-      if (accumulate) {
-        lo += *reinterpret_cast<const f32x4*>(dst);
-        hi += *reinterpret_cast<const f32x4*>(dst + 4);
-      }
-      *reinterpret_cast<f32x4*>(dst) = lo;
-      *reinterpret_cast<f32x4*>(dst + 4) = hi;
-    } else {
-      uint16_t* dst = reinterpret_cast<uint16_t*>(out) + base + f;
-      if (accumulate) {
-        const u32x4 prev = ldg16(dst);
+  }
+  const float inv = 1.0f / wsum;
+  const size_t base = ((size_t)bh * N + qrow) * D + f;
+  const u32x4 gv = ldg16(G + base);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          o[2 * e] += bf_lo(prev[e]);
-          o[2 * e + 1] += bf_hi(prev[e]);
-        }
-      }
-      stg16(dst, (u32x4){pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]), pack_bf16(o[4], o[5]),
-                         pack_bf16(o[6], o[7])});
+  for (int e = 0; e < 4; ++e) {
+    o[2 * e] = (o[2 * e] * inv) * sigmoid(bf_lo(gv[e]));
+    o[2 * e + 1] = (o[2 * e + 1] * inv) * sigmoid(bf_hi(gv[e]));
+  }
+  if (OUT_F32) {
+    float* dst = reinterpret_cast<float*>(out) + base;
+    f32x4 lo = (f32x4){o[0], o[1], o[2], o[3]}, hi = (f32x4){o[4], o[5], o[6], o[7]};
+    if (accumulate) {
+      lo += *reinterpret_cast<const f32x4*>(dst);
+      hi += *reinterpret_cast<const f32x4*>(dst + 4);
     }
+    *reinterpret_cast<f32x4*>(dst) = lo;
+    *reinterpret_cast<f32x4*>(dst + 4) = hi;
+  } else {
+    uint16_t* dst = reinterpret_cast<uint16_t*>(out) + base;
+    if (accumulate) {
+      const u32x4 prev = ldg16(dst);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[2 * e] += bf_lo(prev[e]);
+        o[2 * e + 1] += bf_hi(prev[e]);
+      }
+    }
+    stg16(dst, (u32x4){pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]), pack_bf16(o[4], o[5]),
+                       pack_bf16(o[6], o[7])});
   }
 }
 
@@ -607,14 +610,14 @@ hipError_t launch_d(const hla_dims& d, const void* q, const void* k, const void*
     hipLaunchKernelGGL((anchor_bf16<D, true>), dim3(grid), dim3(kThreads), 0, stream, Qp, Kp, Vp,
                        Gp, vt, out, N, n_pad, nqb, nmain, split, c, accumulate, part, part_ml);
     if (tail > 0)
-      hipLaunchKernelGGL((anchor_combine<D, true>), dim3(tail), dim3(kBR), 0, stream, part,
-                         part_ml, Gp, out, N, nqb, nmain, split, accumulate);
+      hipLaunchKernelGGL((anchor_combine<D, true>), dim3(tail * (D / 8)), dim3(256), 0, stream,
+                         part, part_ml, Gp, out, N, nqb, nmain, split, accumulate);
   } else {
     hipLaunchKernelGGL((anchor_bf16<D, false>), dim3(grid), dim3(kThreads), 0, stream, Qp, Kp, Vp,
                        Gp, vt, out, N, n_pad, nqb, nmain, split, c, accumulate, part, part_ml);
     if (tail > 0)
-      hipLaunchKernelGGL((anchor_combine<D, false>), dim3(tail), dim3(kBR), 0, stream, part,
-                         part_ml, Gp, out, N, nqb, nmain, split, accumulate);
+      hipLaunchKernelGGL((anchor_combine<D, false>), dim3(tail * (D / 8)), dim3(256), 0, stream,
+                         part, part_ml, Gp, out, N, nqb, nmain, split, accumulate);
   }
   return hipGetLastError();
 }

@@ -85,6 +85,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--profile", choices=["anchor", "linear", "step", "copy"], default=None)
     ap.add_argument("--iters", type=int, default=5, help="launches per --profile run")
+    ap.add_argument("--sweep", action="store_true",
+                    help="720p duration sweep: one gated linear and one gated softmax layer per clip "
+                         "length (B=1, H=16), one JSON line each; no contract line")
     return ap.parse_args()
 
 
@@ -151,6 +154,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
+
+    if args.sweep:
+        duration_sweep(torch, hla)
+        return
 
     if args.profile == "copy":
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
@@ -253,6 +260,44 @@ def main():
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+def duration_sweep(torch, hla):
+    """Per-layer time of gated linear vs gated softmax attention as the clip grows.
+
+    A 3:1 hybrid block spends (3 t_linear + t_softmax) / 4 per layer against
+    t_softmax for an all-softmax block; the ratio is the hybrid's speed-up.
+    """
+    from hla_inputs import DURATION_FRAMES, duration_workload
+    for frames, note in DURATION_FRAMES:
+        w = duration_workload(frames)
+        q, k, v, g = gpu_inputs(w, 0, torch)
+        ws_l, ws_a = hla.linear_workspace(q), hla.anchor_workspace(q)
+        out = torch.empty_like(q)
+        res = {"sweep": "720p duration", "frames": frames, "clip": note, "latent_thw": list(w.latent),
+               "B": w.B, "H": w.H, "N": w.N, "D": w.D}
+        for name, fn, reps in (
+                ("linear", lambda: hla.hla_linear_fwd(q, k, v, g, out=out, eps=w.eps, workspace=ws_l), 10),
+                ("softmax", lambda: hla.hla_softmax_anchor_fwd(q, k, v, g, out=out, scale=w.scale,
+                                                               workspace=ws_a), 3)):
+            fn()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            res[f"{name}_ms"] = round(a.elapsed_time(b) / reps, 4)
+        BH, N, D = w.B * w.H, w.N, w.D
+        res["linear_GB_s"] = round(10.0 * N * D * BH / (res["linear_ms"] * 1e-3) / 1e9, 1)
+        res["softmax_TFLOP_s"] = round(4.0 * N * N * D * BH / (res["softmax_ms"] * 1e-3) / 1e12, 1)
+        hyb = (3 * res["linear_ms"] + res["softmax_ms"]) / 4
+        res["hybrid_3to1_ms_per_layer"] = round(hyb, 4)
+        res["speedup_hybrid_vs_all_softmax"] = round(res["softmax_ms"] / hyb, 3)
+        print(json.dumps(res), flush=True)
+        del q, k, v, g, out, ws_l, ws_a
+        torch.cuda.empty_cache()
 
 
 def stack_timing(torch, hla):

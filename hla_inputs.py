@@ -68,6 +68,27 @@ WORKLOADS: List[Workload] = [
 
 BY_NAME = {w.name: w for w in WORKLOADS}
 
+# Duration sweep at 720p (latent grid 23 x 40 per latent frame, T = (frames-1)/4 + 1):
+# the pages report that the hybrid's advantage over full softmax grows with video
+# duration, up to 720p / 60 s. (frames, note) pairs; 961 and 1441 frames are 60 s at
+# 16 and 24 fps.
+DURATION_FRAMES: List[Tuple[int, str]] = [
+    (81, "3.4 s at 24 fps"), (121, "5 s at 24 fps"), (193, "8 s at 24 fps"),
+    (481, "20 s at 24 fps"), (961, "60 s at 16 fps"), (1441, "60 s at 24 fps"),
+]
+
+
+def latent_720p(frames: int) -> Tuple[int, int, int]:
+    """Latent (T, H, W) grid of a 720p clip of ``frames`` frames."""
+    return ((frames - 1) // 4 + 1, 23, 40)
+
+
+def duration_workload(frames: int, B: int = 1, H: int = 16) -> Workload:
+    """A 720p workload of ``frames`` frames (index 6: its own seed range)."""
+    T, Hl, Wl = latent_720p(frames)
+    return Workload(6, f"720p_{frames}f", B, H, T * Hl * Wl, 128, "bf16", (T, Hl, Wl),
+                    note=f"720p x {frames} frames")
+
 
 def seed_for(workload_index: int, layer: int, slot: str) -> int:
     return SEED_BASE + 1000 * workload_index + 10 * layer + SLOT[slot]

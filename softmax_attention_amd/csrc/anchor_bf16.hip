@@ -7,8 +7,8 @@
 //
 // Flash-style single pass: a workgroup owns 256 query rows (8 waves x 32, two
 // waves per SIMD) of one (b, h) and streams all keys through LDS in tiles of
-// 64, double-buffered; the eight waves share each tile, so K and V cross from
-// L2 into LDS once per 256 queries.
+// 64, four buffers deep with one barrier per two tiles; the eight waves share
+// each tile, so K and V cross from L2 into LDS once per 256 queries.
 // Per tile and wave:
 //   S^T = K Q^T      32x32x16 bf16 MFMA, K from LDS, Q^T held in registers; the
 //                    transposed product puts one query per lane (and its
@@ -130,15 +130,38 @@ __global__ __launch_bounds__(kThreads, 1) void anchor_bf16(const uint16_t* __res
   // reads of the other, and does not make every LDS read wait for them.
   __shared__ __attribute__((aligned(16))) uint16_t Ks0[kBC * D];
   __shared__ __attribute__((aligned(16))) uint16_t Ks1[kBC * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks2[kBC * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks3[kBC * D];
   __shared__ __attribute__((aligned(16))) uint16_t Vs0[kBC * D];
   __shared__ __attribute__((aligned(16))) uint16_t Vs1[kBC * D];
-  auto kbuf = [&](auto b_c) -> uint16_t* {
-    if constexpr (decltype(b_c)::value == 0) return Ks0;
-    else return Ks1;
+  __shared__ __attribute__((aligned(16))) uint16_t Vs2[kBC * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs3[kBC * D];
+  // buffer b of each tensor: a compile-time b names one array, which lets the
+  // compiler keep LDS reads of one buffer independent of the DMA into another;
+  // a run-time b (rare edge iterations) selects among them
+  auto kbuf = [&](auto b) -> uint16_t* {
+    if constexpr (std::is_integral_v<decltype(b)>) {
+      const int x = b & 3;
+      return x == 0 ? Ks0 : x == 1 ? Ks1 : x == 2 ? Ks2 : Ks3;
+    } else {
+      constexpr int B = decltype(b)::value & 3;
+      if constexpr (B == 0) return Ks0;
+      else if constexpr (B == 1) return Ks1;
+      else if constexpr (B == 2) return Ks2;
+      else return Ks3;
+    }
   };
-  auto vbuf = [&](auto b_c) -> uint16_t* {
-    if constexpr (decltype(b_c)::value == 0) return Vs0;
-    else return Vs1;
+  auto vbuf = [&](auto b) -> uint16_t* {
+    if constexpr (std::is_integral_v<decltype(b)>) {
+      const int x = b & 3;
+      return x == 0 ? Vs0 : x == 1 ? Vs1 : x == 2 ? Vs2 : Vs3;
+    } else {
+      constexpr int B = decltype(b)::value & 3;
+      if constexpr (B == 0) return Vs0;
+      else if constexpr (B == 1) return Vs1;
+      else if constexpr (B == 2) return Vs2;
+      else return Vs3;
+    }
   };
 
   // The first nmain workgroups each own one query block over all keys. They are
@@ -236,8 +259,7 @@ __global__ __launch_bounds__(kThreads, 1) void anchor_bf16(const uint16_t* __res
   // ---- building blocks -----------------------------------------------------
   // S^T of the tile held in K buffer KB (two 32-key blocks)
   auto s_tile = [&](auto kb_c, f32x16* s) {
-    constexpr int KB = decltype(kb_c)::value;
-    const uint16_t* Kb = kbuf(std::integral_constant<int, KB>{});
+    const uint16_t* Kb = kbuf(kb_c);
     s[0] = (f32x16){};
     s[1] = (f32x16){};
 #pragma unroll
@@ -252,8 +274,7 @@ __global__ __launch_bounds__(kThreads, 1) void anchor_bf16(const uint16_t* __res
   // O^T += V^T P^T for the tile held in V buffer VB; k-slot s of half h is
   // key 16ks + 8(s>>2) + 4h + (s&3)
   auto pv_tile = [&](auto vb_c, const u32x4* pb) {
-    constexpr int VB = decltype(vb_c)::value;
-    const uint16_t* Vb = vbuf(std::integral_constant<int, VB>{});
+    const uint16_t* Vb = vbuf(vb_c);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
@@ -333,75 +354,88 @@ __global__ __launch_bounds__(kThreads, 1) void anchor_bf16(const uint16_t* __res
 
   // ---- software pipeline ------------------------------------------------------
   // Iteration j overlaps the softmax of tile j (VALU) with the MFMAs of P V for
-  // tile j-1 and of S^T for tile j+1, which do not depend on it. K therefore
-  // runs one tile ahead of the softmax and V one tile behind: iteration j reads
-  // K(j+1) from K buffer (j+1)&1 and V(j-1) from V buffer (j-1)&1 while K(j+2)
-  // and V(j) stream into buffers j&1. The accumulator rescale for tile j waits
-  // until P V of tile j-1 has been added.
+  // tile j-1 and of S^T for tile j+1, which do not depend on it: K runs one
+  // tile ahead of the softmax and V one tile behind. The accumulator rescale
+  // for tile j waits until P V of tile j-1 has been added.
   f32x16 s_cur[2];
   u32x4 p_prev[4];
-  auto iteration = [&](auto buf_c, auto steady_c, int j) {
-    constexpr int BUF = decltype(buf_c)::value;
+  // Four K and four V buffers; local tile t lives in buffer t % 4. Iterations go
+  // in pairs: the first of a pair issues K(j+3), K(j+4), V(j+1), V(j+2), the
+  // second ends with the barrier, so each pair reads only tiles issued by the
+  // previous one and overwrites only buffers that pair has finished reading.
+  // jm_c: jl % 4, as a compile-time constant in the unrolled steady loop or
+  // as an int in the few edge iterations
+  auto iteration = [&](auto jm_c, auto steady_c, int jl) __attribute__((always_inline)) {
     constexpr bool STEADY = decltype(steady_c)::value;
-    using Cur = std::integral_constant<int, BUF>;
-    using Oth = std::integral_constant<int, BUF ^ 1>;
-    // S(j) was computed last iteration; re-define it here (an empty asm, no
-    // memory access) so the compiler cannot hoist this iteration's softmax
-    // above the previous barrier, away from the MFMAs it should overlap
+    constexpr bool RT = std::is_integral_v<decltype(jm_c)>;
+    auto shifted = [&](auto d_c) {
+      constexpr int Dd = decltype(d_c)::value;
+      if constexpr (RT) return int((jm_c + Dd) & 3);
+      else return std::integral_constant<int, (decltype(jm_c)::value + Dd) & 3>{};
+    };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    using S3 = std::integral_constant<int, 3>;
+    bool first;
+    if constexpr (RT) first = (jm_c & 1) == 0;
+    else first = (decltype(jm_c)::value & 1) == 0;
+    const int j = t0 + jl;
     asm volatile("" : "+v"(s_cur[0]), "+v"(s_cur[1]));
-    issue(j + 2, j, Cur{});
+    if (first) {
+      load_k(j + 3, shifted(S3{}));
+      load_k(j + 4, shifted(S0{}));
+      load_v(j + 1, shifted(S1{}));
+      load_v(j + 2, shifted(S2{}));
+    }
     u32x4 p_cur[4];
     const bool mask = !STEADY && ragged && j == ntiles - 1;
     const float alpha = softmax(s_cur, p_cur, j, mask);
-    if (STEADY || j > t0) pv_tile(Oth{}, p_prev);
+    if (STEADY || jl > 0) pv_tile(shifted(S3{}), p_prev);
     f32x16 s_next[2];
-    if (STEADY || j + 1 < t1) s_tile(Oth{}, s_next);
-    // and keep P(j) and the row sum from sinking below them: they are used by
-    // the next iteration only, so the compiler would otherwise compute them late
+    if (STEADY || j + 1 < t1) s_tile(shifted(S1{}), s_next);
     asm volatile("" ::"v"(p_cur[0]), "v"(p_cur[1]), "v"(p_cur[2]), "v"(p_cur[3]), "v"(l_run));
     rescale(alpha);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) p_prev[ks] = p_cur[ks];
     s_cur[0] = s_next[0];
     s_cur[1] = s_next[1];
-    wait_all_memory();  // this iteration's tiles have landed in LDS
-    __syncthreads();
-    // keep the next iteration's softmax out of this one: it must stay next to
-    // the MFMAs it is meant to overlap
+    if (!first) {
+      wait_all_memory();  // the pair's tiles have landed in LDS
+      __syncthreads();
+    }
     __builtin_amdgcn_sched_barrier(0);
   };
-  using B0 = std::integral_constant<int, 0>;
-  using B1 = std::integral_constant<int, 1>;
   using Steady = std::true_type;
   using Edge = std::false_type;
-
-  // prologue: K(t0), K(t0+1) in; S^T of tile t0
+  // prologue: K(t0), K(t0+1), K(t0+2), V(t0) in; S^T of tile t0
   const int nt = t1 - t0;
-  load_k(t0, B0{});
-  if (nt > 1) load_k(t0 + 1, B1{});
+  load_k(t0, std::integral_constant<int, 0>{});
+  load_k(t0 + 1, std::integral_constant<int, 1>{});
+  load_k(t0 + 2, std::integral_constant<int, 2>{});
+  load_v(t0, std::integral_constant<int, 0>{});
   wait_all_memory();
   __syncthreads();
-  s_tile(B0{}, s_cur);
-  __syncthreads();  // K buffer 0 is free for K(t0+2)
+  s_tile(std::integral_constant<int, 0>{}, s_cur);
+  __syncthreads();  // K buffer 0 is free for K(t0+4)
 
-  // buffer parity follows the tile's position in the range
-  iteration(B0{}, Edge{}, t0);
+  auto run = [&](int jl, auto steady_c) __attribute__((always_inline)) {
+    iteration(int(jl & 3), steady_c, jl);
+  };
+  iteration(std::integral_constant<int, 0>{}, Edge{}, 0);
   int jl = 1;
-  for (; jl + 2 <= nt - 1; jl += 2) {  // local tiles 1 .. nt-2 are steady
-    iteration(B1{}, Steady{}, t0 + jl);
-    iteration(B0{}, Steady{}, t0 + jl + 1);
+  for (; jl + 4 <= nt - 1; jl += 4) {  // local tiles 1 .. nt-2 are steady
+    iteration(std::integral_constant<int, 1>{}, Steady{}, jl);
+    iteration(std::integral_constant<int, 2>{}, Steady{}, jl + 1);
+    iteration(std::integral_constant<int, 3>{}, Steady{}, jl + 2);
+    iteration(std::integral_constant<int, 0>{}, Steady{}, jl + 3);
   }
-  if (jl <= nt - 2) {
-    iteration(B1{}, Steady{}, t0 + jl);
-    ++jl;
-  }
-  if (jl == nt - 1 && jl > 0) {  // the last tile
-    if (jl & 1) iteration(B1{}, Edge{}, t0 + jl);
-    else iteration(B0{}, Edge{}, t0 + jl);
-  }
+  for (; jl <= nt - 2; ++jl) run(jl, Steady{});
+  if (jl == nt - 1 && jl > 0) run(jl, Edge{});
+  // an odd-length range ends on the first iteration of a pair: no barrier was
+  // needed after it, and none is needed now (only registers remain)
   // P V of the last tile
-  if ((nt - 1) & 1) pv_tile(B1{}, p_prev);
-  else pv_tile(B0{}, p_prev);
+  pv_tile(int((nt - 1) & 3), p_prev);
 
   if (piece >= 0) {
     // partial result of a key range: unnormalised O, running max and row sum

@@ -289,3 +289,26 @@ def test_duration_sweep_longest_sampled():
     print(f"[{w.name}] linear err {e_lin:.3e}  softmax err {e_sm:.3e} on {len(rows)} rows", flush=True)
     assert e_lin <= TOL[torch.bfloat16]
     assert e_sm <= TOL[torch.bfloat16]
+
+
+def test_hybrid_stack_bf16_residual_and_d64():
+    # the stack with a bf16 residual stream (rounded after every layer) and with
+    # head dim 64; delta = x_L - x_0 against the per-layer oracle sum
+    kinds = oracle.hybrid_kinds(4)
+    for (B, H, N, D, xdt, seed) in [(1, 2, 700, 128, torch.bfloat16, 7300),
+                                    (2, 2, 333, 64, torch.float32, 7400)]:
+        layers = [make((B, H, N, D), seed + 10 * l, torch.bfloat16) for l in range(4)]
+        x0 = custom((B, H, N, D), seed + 99, torch.float32, n=1)[0].to(xdt)
+        x = x0.to(DEV)
+        hla.hla_hybrid_stack_fwd(x, [tuple(t.to(DEV) for t in L) for L in layers], kinds)
+        torch.cuda.synchronize()
+        ref = oracle.hybrid_stack(x0.float(), layers, kinds, 1e-6, D ** -0.5) - oracle.as_f64(x0.float())
+        delta = x.float().cpu() - x0.float()
+        # a bf16 residual adds one rounding of |x| ~ 1 per layer: half an ulp of 2^-8
+        # per layer, far above the layer outputs themselves, so judge it against
+        # the rounding bound instead of the relative metric
+        if xdt == torch.bfloat16:
+            bound = 4 * 2.0 ** -8 * float(x0.float().abs().max())
+            assert float((delta - torch.from_numpy(ref).float()).abs().max()) <= bound
+        else:
+            assert rel_err(delta, ref) <= TOL[torch.bfloat16]

@@ -15,13 +15,14 @@ What the pages state (SANA-Video 2.0, five web summaries of one paper):
     attention section);
   * softmax anchors keep exact, full-rank token interactions (lode.cx article,
     "The Core Innovation").
-The pages give no formula for either operator. The readings used here, each
-listed in DESIGN.md, are:
+The pages give no formula for either operator. The readings used here are:
   phi(x)   = max(x, 0)                         (ReLU feature map)
   sigma(x) = 1 / (1 + exp(-x))                 (sigmoid output gate, per channel)
   linear : S = phi(K)^T V, z = phi(K)^T 1,  O = sigma(G) * (phi(Q) S) / (phi(Q) z + eps)
   softmax: O = sigma(G) * softmax_rows(s Q K^T) V,  s = 1/sqrt(D), non-causal
   stack  : x_l = x_{l-1} + layer_l(Q_l, K_l, V_l, G_l), kinds L,L,L,S repeating
+  write  : linear attention whose state takes beta_m = sigma(W_m) of each token's
+           phi(K_m) (in S and in z), W one logit per token and head
 Every array is float64; bf16 or fp32 inputs are upcast exactly.
 """
 from __future__ import annotations
@@ -77,6 +78,30 @@ def gated_linear(q, k, v, g, eps: float):
     q = as_f64(q)
     g = as_f64(g)
     S, z = linear_state(k, v)
+    phq = relu(q)
+    num = np.matmul(phq, S)
+    den = np.matmul(phq, z[..., :, None])[..., 0] + float(eps)
+    return sigmoid(g) * num / den[..., None]
+
+
+def gated_linear_write(q, k, v, g, w, eps: float):
+    """Gated linear attention with a write gate on the state (O(N) form).
+
+    The ai-papers.net summary (section on hybrid linear attention) describes a
+    gate that regulates how much each token writes into the fixed-size state;
+    the pages give no formula. Reading used here: one write strength per token
+    and head, beta_m = sigma(W_m), scales the token's key feature in both the
+    state and the normaliser, so a token with beta = 0 is as if absent:
+      S = sum_m beta_m phi(K_m)^T V_m,  z = sum_m beta_m phi(K_m)
+      O_n = sigma(G_n) * (phi(Q_n) S) / (phi(Q_n) . z + eps)
+    w: [..., N] (the gate logits W).
+    """
+    q = as_f64(q)
+    g = as_f64(g)
+    beta = sigmoid(as_f64(w))
+    phk = beta[..., :, None] * relu(as_f64(k))
+    S = np.matmul(np.swapaxes(phk, -1, -2), as_f64(v))
+    z = phk.sum(axis=-2)
     phq = relu(q)
     num = np.matmul(phq, S)
     den = np.matmul(phq, z[..., :, None])[..., 0] + float(eps)

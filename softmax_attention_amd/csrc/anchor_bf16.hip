@@ -40,7 +40,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kBR = 32 * kWaves;        // query rows per workgroup
 constexpr int kBC = 64;   // keys per LDS tile
 constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
-constexpr int kMaxPieces = 256;  // most key-range pieces one call splits its last round into
+constexpr int kMaxPieces = 256;  // most key-range pieces one call splits its last batch into
 
 // LDS tiles use XOR swizzles of whole 16-byte chunks instead of padding:
 //   K   (row = key, D/8 chunks): chunk c of row k sits at c ^ (k & 15)
@@ -169,7 +169,7 @@ __global__ __launch_bounds__(kThreads, 1) void anchor_bf16(const uint16_t* __res
   // contiguous range of (b, h, query block) and the query blocks of one head
   // share that XCD's L2 while streaming its K and V. The workgroups after them
   // (dispatched last) split each remaining query block into `split` key ranges,
-  // so the last round of workgroups is short; they leave unnormalised partial
+  // so the last batch of workgroups is short; they leave unnormalised partial
   // results in `part` for anchor_combine.
   const int bid = blockIdx.x;
   int logical, piece = -1;
@@ -618,8 +618,8 @@ hipError_t launch_d(const hla_dims& d, const void* q, const void* k, const void*
   uint16_t* vt = reinterpret_cast<uint16_t*>(w);
   float* part = reinterpret_cast<float*>(w + L.part_off);
   float* part_ml = reinterpret_cast<float*>(w + L.ml_off);
-  // Workgroups run one round per CU at a time. The query blocks of an
-  // incomplete last round are split along the keys so that round takes a
+  // Workgroups run in batches of one per CU. The query blocks of an
+  // incomplete last batch are split along the keys so that batch takes a
   // fraction of a full one.
   const int slots = device_cus();
   int tail = total % slots, split = 1;

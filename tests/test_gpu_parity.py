@@ -260,7 +260,7 @@ def test_hybrid_stack_workload_sampled():
 
 
 def test_softmax_split_last_round_full():
-    # 24 query blocks of 256 rows leave the last round of workgroups incomplete,
+    # 24 query blocks of 256 rows leave the last batch of workgroups incomplete,
     # so every block is split along the keys and merged by the combine kernel;
     # checked in full, plain and accumulating into fp32
     B, H, N, D = 1, 3, 2000, 128

@@ -152,3 +152,62 @@ def test_linear_mutant_is_caught(mutant):
                                     sm_transposed_v, sm_scale_sqrt_wrong])
 def test_softmax_mutant_is_caught(mutant):
     assert softmax_checks(mutant) > 0, mutant.__name__
+
+
+# --- write-gated linear mutants -------------------------------------------------
+
+from tests.test_oracle_pins import brute_linear_write  # noqa: E402
+
+
+def wl_ok(q, k, v, g, w, eps):
+    return oracle.gated_linear_write(q, k, v, g, w, eps)
+
+
+def _wl(q, k, v, g, eps, bs, bz, bq=None):
+    phk = relu(k)
+    S = np.swapaxes(bs[..., :, None] * phk, -1, -2) @ v
+    z = (bz[..., :, None] * phk).sum(-2)
+    phq = relu(q) if bq is None else bq[..., :, None] * relu(q)
+    return sig(g) * (phq @ S) / ((phq @ z[..., None]) + eps)
+
+
+def wl_state_only(q, k, v, g, w, eps):       # beta in S, not in the normaliser
+    return _wl(q, k, v, g, eps, sig(w), np.ones_like(w))
+
+
+def wl_norm_only(q, k, v, g, w, eps):        # beta in the normaliser only
+    return _wl(q, k, v, g, eps, np.ones_like(w), sig(w))
+
+
+def wl_on_queries(q, k, v, g, w, eps):       # beta applied to the query rows
+    return _wl(q, k, v, g, eps, np.ones_like(w), np.ones_like(w), sig(w))
+
+
+def wl_no_sigmoid(q, k, v, g, w, eps):       # raw logits as strengths
+    return _wl(q, k, v, g, eps, w, w)
+
+
+def write_checks(f):
+    fails = 0
+    for (N, D, eps, seed) in [(9, 5, 0.3, 900), (20, 8, 1e-6, 910)]:
+        q, k, v, g = (rand((1, 1, N, D), seed + i) for i in range(4))
+        w = rand((1, 1, N), seed + 4, scale=2.0)
+        try:
+            with np.errstate(all="ignore"):
+                got = f(q, k, v, g, w, eps)
+            ref = np.array(brute_linear_write(q[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist(),
+                                              g[0, 0].tolist(), w[0, 0].tolist(), eps))
+            if not np.allclose(got[0, 0], ref, rtol=1e-10, atol=1e-12):
+                fails += 1
+        except Exception:
+            fails += 1
+    return fails
+
+
+def test_correct_write_gated_oracle_passes_checks():
+    assert write_checks(wl_ok) == 0
+
+
+@pytest.mark.parametrize("mutant", [wl_state_only, wl_norm_only, wl_on_queries, wl_no_sigmoid])
+def test_write_gated_mutant_is_caught(mutant):
+    assert write_checks(mutant) > 0, mutant.__name__

@@ -351,3 +351,78 @@ def test_max_rel_error_metric():
     assert abs(oracle.max_rel_error(got, ref) - 1e-2) < 1e-15
     got[0, 1, 1, 1] = np.nan
     assert oracle.max_rel_error(got, ref) == float("inf")
+
+
+# ----------------------------------------------------------------------------
+# write-gated linear attention (beta_m = sigma(W_m) on each token's phi(K_m))
+# ----------------------------------------------------------------------------
+
+def brute_linear_write(q, k, v, g, w, eps):
+    """O_n = sig(G_n) * sum_m b_m a_nm V_m / (sum_m b_m a_nm + eps), a_nm = phi(Q_n).phi(K_m)."""
+    N, D = len(q), len(q[0])
+    out = [[0.0] * D for _ in range(N)]
+    for n in range(N):
+        a = []
+        for m in range(N):
+            s = 0.0
+            for d in range(D):
+                s += max(q[n][d], 0.0) * max(k[m][d], 0.0)
+            a.append(_sig(w[m]) * s)
+        den = sum(a) + eps
+        for j in range(D):
+            num = 0.0
+            for m in range(N):
+                num += a[m] * v[m][j]
+            out[n][j] = _sig(g[n][j]) * num / den
+    return out
+
+
+@pytest.mark.parametrize("N,D,eps", [(1, 4, 1e-6), (9, 5, 0.3), (40, 16, 1e-6)])
+def test_write_gated_linear_matches_brute_force(N, D, eps):
+    q, k, v, g = (rand((N, D), seed=60 + i) for i in range(4))
+    w = rand((N,), seed=64, scale=2.0)
+    ref = brute_linear_write(q.tolist(), k.tolist(), v.tolist(), g.tolist(), w.tolist(), eps)
+    assert _close(oracle.gated_linear_write(q, k, v, g, w, eps), ref)
+
+
+def test_write_gate_open_is_plain_gated_linear():
+    # W = +inf writes every token in full (beta = 1): the plain operator
+    q, k, v, g = (rand((2, 3, 50, 8), seed=70 + i) for i in range(4))
+    w = np.full((2, 3, 50), np.inf)
+    assert np.array_equal(oracle.gated_linear_write(q, k, v, g, w, 1e-6),
+                          oracle.gated_linear(q, k, v, g, 1e-6))
+
+
+def test_write_gate_closed_removes_tokens():
+    # W = -inf (beta = 0) for a token is the same as leaving its K, V out
+    q, k, v, g = (rand((1, 2, 30, 8), seed=80 + i) for i in range(4))
+    keep = np.arange(30) % 3 != 1
+    w = np.where(keep, np.inf, -np.inf)[None, None, :].repeat(2, axis=1)
+    got = oracle.gated_linear_write(q, k, v, g, w, 1e-6)
+    # queries keep all rows; keys and values only the written tokens
+    phq = np.maximum(q, 0.0)
+    phk = np.maximum(k[..., keep, :], 0.0)
+    S = np.swapaxes(phk, -1, -2) @ v[..., keep, :]
+    z = phk.sum(axis=-2)
+    ref = (1 / (1 + np.exp(-g))) * (phq @ S) / ((phq @ z[..., :, None]) + 1e-6)
+    assert _close(got, ref)
+
+
+def test_write_gate_common_strength_scales_eps():
+    # one beta for every token cancels between state and normaliser except against
+    # eps: the result equals the plain operator with eps / beta
+    q, k, v, g = (rand((1, 1, 64, 16), seed=90 + i) for i in range(4))
+    wl = 0.7
+    beta = 1 / (1 + math.exp(-wl))
+    got = oracle.gated_linear_write(q, k, v, g, np.full((1, 1, 64), wl), 0.05)
+    assert _close(got, oracle.gated_linear(q, k, v, g, 0.05 / beta))
+
+
+def test_write_gated_quadratic_closed_form():
+    # O = sig(G) (A V) / (A 1 + eps) with A = phi(Q) diag(beta) phi(K)^T
+    q, k, v, g = (rand((2, 2, 300, 32), seed=100 + i) for i in range(4))
+    w = rand((2, 2, 300), seed=104, scale=3.0)
+    beta = 1 / (1 + np.exp(-w))
+    A = np.maximum(q, 0) @ (beta[..., :, None] * np.maximum(k, 0)).swapaxes(-1, -2)
+    ref = (1 / (1 + np.exp(-g))) * (A @ v) / (A.sum(axis=-1, keepdims=True) + 1e-6)
+    assert _close(oracle.gated_linear_write(q, k, v, g, w, 1e-6), ref, tol=1e-11)

@@ -241,6 +241,23 @@ def main():
                                "pipeline, not this attention path)"),
     }
 
+    # write-gated variant of the linear layer (one write logit per token and head)
+    wg = [torch.randn((w.B, w.H, w.N), device=dev).to(torch.bfloat16) for _ in range(2)]
+    for i in range(2):
+        hla.hla_linear_write_gated_fwd(*sets[i], wg[i], out=outs[0], eps=w.eps, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(K):
+        hla.hla_linear_write_gated_fwd(*sets[i % 2], wg[i % 2], out=outs[0], eps=w.eps, workspace=ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wg_ms = e0.elapsed_time(e1) / K
+    wg_bytes = lin_bytes + 2.0 * N * BH
+    details["linear_write_gated"] = {"ms": round(wg_ms, 4), "GB_s": round(wg_bytes / (wg_ms * 1e-3) / 1e9, 1),
+                                     "frac_hbm_peak": round(wg_bytes / (wg_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                                     "note": "back-to-back calls (each pays the previous call's write-back)"}
+
     if not args.no_stack:
         details["stack"] = stack_timing(torch, hla)
 

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define HLA_ABI_VERSION 2
+#define HLA_ABI_VERSION 3
 
 typedef enum { HLA_F32 = 0, HLA_BF16 = 1 } hla_dtype;
 
@@ -95,6 +95,21 @@ size_t hla_linear_workspace_bytes(const hla_dims* d);
 hla_status hla_linear_fwd(const hla_dims* d, const void* q, const void* k, const void* v,
                           const void* g, void* out, int accumulate, float eps, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/* Write-gated linear attention: as hla_linear_fwd, but each token writes into the
+ * state with strength beta_n = sigma(W_n), one logit per token and head:
+ *   S = sum_n beta_n phi(K_n)^T V_n,  z = sum_n beta_n phi(K_n)
+ *   O_n = sigma(G_n) (.) (phi(Q_n) S) / (phi(Q_n) . z + eps)
+ * (the gate that regulates what is written into the fixed-size state, ai-papers.net
+ * summary, section on hybrid linear attention; the pages give no formula, this is
+ * one reading of it). `w` is a device tensor [B, H, N], contiguous, dtype
+ * d->in_dtype, 16-byte aligned; W = +inf reproduces hla_linear_fwd exactly, W = -inf
+ * removes the token. Workspace, accumulate, eps and errors as in hla_linear_fwd
+ * (HLA_ERR_NULL_PTR / HLA_ERR_ALIGN also for `w`). */
+hla_status hla_linear_write_gated_fwd(const hla_dims* d, const void* q, const void* k,
+                                      const void* v, const void* g, const void* w, void* out,
+                                      int accumulate, float eps, void* workspace,
+                                      size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace hla_softmax_anchor_fwd needs for `d`: on the bf16
  * path a repacked copy of V (B*H*D*ceil(N/64)*64 bf16, V transposed with zero

@@ -27,7 +27,8 @@ STATUS = {
     4: "HLA_ERR_BAD_ARG", 5: "HLA_ERR_ALIGN", 6: "HLA_ERR_WORKSPACE", 7: "HLA_ERR_HIP",
 }
 EXPORTS = ("hla_abi_version", "hla_status_str", "hla_linear_workspace_bytes", "hla_linear_fwd",
-           "hla_softmax_anchor_workspace_bytes", "hla_softmax_anchor_fwd", "hla_hybrid_stack_fwd")
+           "hla_linear_write_gated_fwd", "hla_softmax_anchor_workspace_bytes",
+           "hla_softmax_anchor_fwd", "hla_hybrid_stack_fwd")
 
 
 class hla_dims(ctypes.Structure):
@@ -75,6 +76,9 @@ def _load() -> ctypes.CDLL:
     lib.hla_linear_fwd.restype = ctypes.c_int
     lib.hla_linear_fwd.argtypes = [pd, P, P, P, P, P, ctypes.c_int, ctypes.c_float, P,
                                    ctypes.c_size_t, P]
+    lib.hla_linear_write_gated_fwd.restype = ctypes.c_int
+    lib.hla_linear_write_gated_fwd.argtypes = [pd, P, P, P, P, P, P, ctypes.c_int, ctypes.c_float,
+                                               P, ctypes.c_size_t, P]
     lib.hla_softmax_anchor_workspace_bytes.restype = ctypes.c_size_t
     lib.hla_softmax_anchor_workspace_bytes.argtypes = [pd]
     lib.hla_softmax_anchor_fwd.restype = ctypes.c_int
@@ -203,6 +207,32 @@ def hla_linear_fwd(q, k, v, g, out=None, accumulate: bool = False, eps: float = 
                             out.data_ptr(), int(bool(accumulate)), float(eps), workspace.data_ptr(),
                             workspace.numel() * workspace.element_size(), _stream(stream))
     _raise("hla_linear_fwd", st)
+    return out
+
+
+def hla_linear_write_gated_fwd(q, k, v, g, w, out=None, accumulate: bool = False,
+                               eps: float = 1e-6, workspace=None, stream=None):
+    """Write-gated linear attention: token n enters the state with sigma(w_n); returns out.
+
+    w has shape [B, H, N] and the dtype of q."""
+    torch = _torch()
+    _check(q, k, v, g)
+    if tuple(w.shape) != tuple(q.shape[:-1]) or w.dtype != q.dtype or not w.is_contiguous():
+        raise ValueError("w must be a contiguous [B, H, N] tensor of q's dtype")
+    if not w.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if out is None:
+        out = torch.empty_like(q)
+    _check(q, out)
+    d = dims_of(q, out.dtype)
+    if workspace is None:
+        workspace = linear_workspace(q, out.dtype)
+    st = lib.hla_linear_write_gated_fwd(ctypes.byref(d), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                        g.data_ptr(), w.data_ptr(), out.data_ptr(),
+                                        int(bool(accumulate)), float(eps), workspace.data_ptr(),
+                                        workspace.numel() * workspace.element_size(),
+                                        _stream(stream))
+    _raise("hla_linear_write_gated_fwd", st)
     return out
 
 

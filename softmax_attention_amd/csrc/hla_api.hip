@@ -108,6 +108,31 @@ LinearPlan linear_plan(const hla_dims& d) {
 
 using namespace hla;
 
+// Checks and launch shared by the plain and the write-gated linear entry points.
+static hla_status linear_common(const hla_dims* d, const void* q, const void* k, const void* v,
+                                const void* g, const void* w, bool gated, void* out,
+                                int accumulate, float eps, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  hla_status st = check_dims(d);
+  if (st != HLA_OK) return st;
+  if (!isfinite(eps) || eps < 0.f || (accumulate != 0 && accumulate != 1)) return HLA_ERR_BAD_ARG;
+  if (empty(d)) return HLA_OK;
+  if ((st = check_tensors(q, k, v, g, out)) != HLA_OK) return st;
+  if (gated) {
+    if (!w) return HLA_ERR_NULL_PTR;
+    if (!aligned16(w)) return HLA_ERR_ALIGN;
+  }
+  const LinearPlan plan = linear_plan(*d);
+  if (!workspace) return HLA_ERR_NULL_PTR;
+  if (!aligned16(workspace)) return HLA_ERR_ALIGN;
+  if (workspace_bytes < plan.total) return HLA_ERR_WORKSPACE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  clear_pending_error();
+  if (d->in_dtype == HLA_BF16)
+    return from_hip(launch_linear_bf16(*d, q, k, v, g, w, out, accumulate, eps, workspace, plan, s));
+  return from_hip(launch_linear_f32(*d, q, k, v, g, w, out, accumulate, eps, workspace, plan, s));
+}
+
 extern "C" {
 
 int hla_abi_version(void) { return HLA_ABI_VERSION; }
@@ -139,20 +164,16 @@ size_t hla_softmax_anchor_workspace_bytes(const hla_dims* d) {
 hla_status hla_linear_fwd(const hla_dims* d, const void* q, const void* k, const void* v,
                           const void* g, void* out, int accumulate, float eps, void* workspace,
                           size_t workspace_bytes, void* stream) {
-  hla_status st = check_dims(d);
-  if (st != HLA_OK) return st;
-  if (!isfinite(eps) || eps < 0.f || (accumulate != 0 && accumulate != 1)) return HLA_ERR_BAD_ARG;
-  if (empty(d)) return HLA_OK;
-  if ((st = check_tensors(q, k, v, g, out)) != HLA_OK) return st;
-  const LinearPlan plan = linear_plan(*d);
-  if (!workspace) return HLA_ERR_NULL_PTR;
-  if (!aligned16(workspace)) return HLA_ERR_ALIGN;
-  if (workspace_bytes < plan.total) return HLA_ERR_WORKSPACE;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  clear_pending_error();
-  if (d->in_dtype == HLA_BF16)
-    return from_hip(launch_linear_bf16(*d, q, k, v, g, out, accumulate, eps, workspace, plan, s));
-  return from_hip(launch_linear_f32(*d, q, k, v, g, out, accumulate, eps, workspace, plan, s));
+  return linear_common(d, q, k, v, g, nullptr, false, out, accumulate, eps, workspace,
+                       workspace_bytes, stream);
+}
+
+hla_status hla_linear_write_gated_fwd(const hla_dims* d, const void* q, const void* k,
+                                      const void* v, const void* g, const void* w, void* out,
+                                      int accumulate, float eps, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  return linear_common(d, q, k, v, g, w, true, out, accumulate, eps, workspace, workspace_bytes,
+                       stream);
 }
 
 hla_status hla_softmax_anchor_fwd(const hla_dims* d, const void* q, const void* k, const void* v,
@@ -214,8 +235,8 @@ hla_status hla_hybrid_stack_fwd(const hla_dims* d, int n_layers, const int32_t* 
   for (int l = 0; l < n_layers; ++l) {
     hipError_t e;
     if (kinds[l] == HLA_LAYER_LINEAR)
-      e = bf ? launch_linear_bf16(*d, q[l], k[l], v[l], g[l], x, 1, eps, workspace, plan, s)
-             : launch_linear_f32(*d, q[l], k[l], v[l], g[l], x, 1, eps, workspace, plan, s);
+      e = bf ? launch_linear_bf16(*d, q[l], k[l], v[l], g[l], nullptr, x, 1, eps, workspace, plan, s)
+             : launch_linear_f32(*d, q[l], k[l], v[l], g[l], nullptr, x, 1, eps, workspace, plan, s);
     else
       e = bf ? launch_anchor_bf16(*d, q[l], k[l], v[l], g[l], x, 1, scale, workspace, s)
              : launch_anchor_f32(*d, q[l], k[l], v[l], g[l], x, 1, scale, s);

@@ -29,12 +29,13 @@ struct Tuning {
 };
 Tuning& tuning();
 
+// w: write-gate logits [B,H,N] (in_dtype) for the write-gated variant, or NULL
 hipError_t launch_linear_bf16(const hla_dims& d, const void* q, const void* k, const void* v,
-                              const void* g, void* out, int accumulate, float eps, void* ws,
-                              const LinearPlan& plan, hipStream_t stream);
+                              const void* g, const void* w, void* out, int accumulate, float eps,
+                              void* ws, const LinearPlan& plan, hipStream_t stream);
 hipError_t launch_linear_f32(const hla_dims& d, const void* q, const void* k, const void* v,
-                             const void* g, void* out, int accumulate, float eps, void* ws,
-                             const LinearPlan& plan, hipStream_t stream);
+                             const void* g, const void* w, void* out, int accumulate, float eps,
+                             void* ws, const LinearPlan& plan, hipStream_t stream);
 // Workspace of the bf16 anchor: V repacked as V^T per head, keys padded to 64.
 size_t anchor_workspace_bytes(const hla_dims& d);
 hipError_t launch_anchor_bf16(const hla_dims& d, const void* q, const void* k, const void* v,

@@ -29,9 +29,13 @@ constexpr int kTile = 64;  // tokens per LDS tile in the state pass
 // 32-column blocks [(w&1)*RB, +RB). MFMA operand A is phi(K)^T (rows = features,
 // k = tokens) and B is V (k = tokens, cols = features); both read 8 tokens of one
 // feature per lane out of a row-major LDS tile.
-template <int D>
+// With WG (the write-gated variant) each token's phi(K) row is first scaled by
+// its write strength sigma(W_n), W one bf16 logit per token and head ([B,H,N]);
+// the scaled row, rounded to bf16, feeds both the MFMA and the normaliser sum.
+template <int D, bool WG>
 __global__ __launch_bounds__(256) void linear_state_bf16(const uint16_t* __restrict__ K,
                                                          const uint16_t* __restrict__ V,
+                                                         const uint16_t* __restrict__ W,
                                                          float* __restrict__ part, int N, int T,
                                                          int C) {
   constexpr int CH = D / 8;                // 16-byte chunks per token row
@@ -50,6 +54,8 @@ __global__ __launch_bounds__(256) void linear_state_bf16(const uint16_t* __restr
   const uint16_t* Vh = V + base;
 
   u32x4 kr[LOADS], vr[LOADS];
+  uint16_t wr[LOADS];
+  const uint16_t* Wh = WG ? W + (size_t)bh * N : nullptr;
   float zacc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) zacc[e] = 0.f;
@@ -67,9 +73,11 @@ __global__ __launch_bounds__(256) void linear_state_bf16(const uint16_t* __restr
       if (n < n1) {
         kr[i] = ldg16_stream(Kh + (size_t)n * D + col);
         vr[i] = ldg16_stream(Vh + (size_t)n * D + col);
+        if (WG) wr[i] = Wh[n];
       } else {
         kr[i] = (u32x4){0, 0, 0, 0};
         vr[i] = (u32x4){0, 0, 0, 0};
+        if (WG) wr[i] = 0;
       }
     }
   };
@@ -85,7 +93,12 @@ __global__ __launch_bounds__(256) void linear_state_bf16(const uint16_t* __restr
     for (int i = 0; i < LOADS; ++i) {
       const int chunk = tid + 256 * i;
       const int row = chunk / CH, col = (chunk % CH) * 8;
-      const u32x4 kk = relu_bf16x8(kr[i]);
+      u32x4 kk = relu_bf16x8(kr[i]);
+      if (WG) {
+        const float beta = sigmoid(bf16_to_f32(wr[i]));
+#pragma unroll
+        for (int p = 0; p < 4; ++p) kk[p] = pack_bf16(bf_lo(kk[p]) * beta, bf_hi(kk[p]) * beta);
+      }
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         zacc[2 * p] += bf_lo(kk[p]);
@@ -345,15 +358,20 @@ __global__ __launch_bounds__(256, 2) void linear_out_bf16(const uint16_t* __rest
 
 template <int D>
 hipError_t launch_d(const hla_dims& d, const void* q, const void* k, const void* v, const void* g,
-                    void* out, int accumulate, float eps, void* ws, const LinearPlan& plan,
-                    hipStream_t stream) {
+                    const void* w, void* out, int accumulate, float eps, void* ws,
+                    const LinearPlan& plan, hipStream_t stream) {
   const int BH = int(d.B * d.H), N = int(d.N);
-  char* w = reinterpret_cast<char*>(ws);
-  float* part = reinterpret_cast<float*>(w + plan.part_off);
-  uint32_t* state = reinterpret_cast<uint32_t*>(w + plan.state_off);
-  hipLaunchKernelGGL(linear_state_bf16<D>, dim3(plan.C, BH), dim3(256), 0, stream,
-                     reinterpret_cast<const uint16_t*>(k), reinterpret_cast<const uint16_t*>(v),
-                     part, N, plan.T, plan.C);
+  char* wsb = reinterpret_cast<char*>(ws);
+  float* part = reinterpret_cast<float*>(wsb + plan.part_off);
+  uint32_t* state = reinterpret_cast<uint32_t*>(wsb + plan.state_off);
+  if (w)
+    hipLaunchKernelGGL((linear_state_bf16<D, true>), dim3(plan.C, BH), dim3(256), 0, stream,
+                       reinterpret_cast<const uint16_t*>(k), reinterpret_cast<const uint16_t*>(v),
+                       reinterpret_cast<const uint16_t*>(w), part, N, plan.T, plan.C);
+  else
+    hipLaunchKernelGGL((linear_state_bf16<D, false>), dim3(plan.C, BH), dim3(256), 0, stream,
+                       reinterpret_cast<const uint16_t*>(k), reinterpret_cast<const uint16_t*>(v),
+                       nullptr, part, N, plan.T, plan.C);
   hipLaunchKernelGGL(linear_reduce_bf16<D>, dim3(D * D / 8 / 256 + 1, BH), dim3(256), 0, stream,
                      part, state, plan.C);
   if (d.out_dtype == HLA_F32)
@@ -370,10 +388,10 @@ hipError_t launch_d(const hla_dims& d, const void* q, const void* k, const void*
 }  // namespace
 
 hipError_t launch_linear_bf16(const hla_dims& d, const void* q, const void* k, const void* v,
-                              const void* g, void* out, int accumulate, float eps, void* ws,
-                              const LinearPlan& plan, hipStream_t stream) {
-  if (d.D == 128) return launch_d<128>(d, q, k, v, g, out, accumulate, eps, ws, plan, stream);
-  return launch_d<64>(d, q, k, v, g, out, accumulate, eps, ws, plan, stream);
+                              const void* g, const void* w, void* out, int accumulate, float eps,
+                              void* ws, const LinearPlan& plan, hipStream_t stream) {
+  if (d.D == 128) return launch_d<128>(d, q, k, v, g, w, out, accumulate, eps, ws, plan, stream);
+  return launch_d<64>(d, q, k, v, g, w, out, accumulate, eps, ws, plan, stream);
 }
 
 }  // namespace hla

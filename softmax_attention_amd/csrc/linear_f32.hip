@@ -12,10 +12,13 @@ namespace {
 
 constexpr int kTileF = 32;  // tokens per LDS tile
 
-// partial S_c = phi(K_c)^T V_c and z_c; thread (ty, tx) owns an R x R block of S
+// partial S_c = phi(K_c)^T V_c and z_c; thread (ty, tx) owns an R x R block of S.
+// W (optional, [B,H,N]): write-gate logits; token n's phi(K_n) is scaled by
+// sigma(W_n) in both S and z.
 template <int D>
 __global__ __launch_bounds__(256) void linear_state_f32(const float* __restrict__ K,
                                                         const float* __restrict__ V,
+                                                        const float* __restrict__ W,
                                                         float* __restrict__ part, int N, int T,
                                                         int C) {
   constexpr int R = D / 16;
@@ -37,7 +40,8 @@ __global__ __launch_bounds__(256) void linear_state_f32(const float* __restrict_
     __syncthreads();
     for (int e = tid; e < kTileF * D; e += 256) {
       const int row = e / D, col = e % D, n = t0 + row;
-      Ks[row][col] = n < n1 ? fmaxf(K[base + (size_t)n * D + col], 0.f) : 0.f;
+      const float beta = (W != nullptr && n < n1) ? sigmoid(W[(size_t)bh * N + n]) : 1.f;
+      Ks[row][col] = n < n1 ? fmaxf(K[base + (size_t)n * D + col], 0.f) * beta : 0.f;
       Vs[row][col] = n < n1 ? V[base + (size_t)n * D + col] : 0.f;
     }
     __syncthreads();
@@ -130,15 +134,15 @@ __global__ __launch_bounds__(256) void linear_out_f32(const float* __restrict__ 
 
 template <int D>
 hipError_t launch_d(const hla_dims& d, const void* q, const void* k, const void* v, const void* g,
-                    void* out, int accumulate, float eps, void* ws, const LinearPlan& plan,
-                    hipStream_t stream) {
+                    const void* wg, void* out, int accumulate, float eps, void* ws,
+                    const LinearPlan& plan, hipStream_t stream) {
   const int BH = int(d.B * d.H), N = int(d.N);
   char* w = reinterpret_cast<char*>(ws);
   float* part = reinterpret_cast<float*>(w + plan.part_off);
   float* state = reinterpret_cast<float*>(w + plan.state_off);
   hipLaunchKernelGGL(linear_state_f32<D>, dim3(plan.C, BH), dim3(256), 0, stream,
-                     reinterpret_cast<const float*>(k), reinterpret_cast<const float*>(v), part, N,
-                     plan.T, plan.C);
+                     reinterpret_cast<const float*>(k), reinterpret_cast<const float*>(v),
+                     reinterpret_cast<const float*>(wg), part, N, plan.T, plan.C);
   hipLaunchKernelGGL(linear_reduce_f32<D>, dim3((D * D + D + 255) / 256, BH), dim3(256), 0,
                      stream, part, state, plan.C);
   hipLaunchKernelGGL(linear_out_f32<D>, dim3((N + 31) / 32, BH), dim3(256), 0, stream,
@@ -150,12 +154,12 @@ hipError_t launch_d(const hla_dims& d, const void* q, const void* k, const void*
 }  // namespace
 
 hipError_t launch_linear_f32(const hla_dims& d, const void* q, const void* k, const void* v,
-                             const void* g, void* out, int accumulate, float eps, void* ws,
-                             const LinearPlan& plan, hipStream_t stream) {
+                             const void* g, const void* w, void* out, int accumulate, float eps,
+                             void* ws, const LinearPlan& plan, hipStream_t stream) {
   switch (d.D) {
-    case 32: return launch_d<32>(d, q, k, v, g, out, accumulate, eps, ws, plan, stream);
-    case 64: return launch_d<64>(d, q, k, v, g, out, accumulate, eps, ws, plan, stream);
-    default: return launch_d<128>(d, q, k, v, g, out, accumulate, eps, ws, plan, stream);
+    case 32: return launch_d<32>(d, q, k, v, g, w, out, accumulate, eps, ws, plan, stream);
+    case 64: return launch_d<64>(d, q, k, v, g, w, out, accumulate, eps, ws, plan, stream);
+    default: return launch_d<128>(d, q, k, v, g, w, out, accumulate, eps, ws, plan, stream);
   }
 }
 

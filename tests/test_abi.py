@@ -38,6 +38,12 @@ def lin(d, q=FAKE, k=FAKE, v=FAKE, g=FAKE, out=FAKE, acc=0, eps=1e-6, ws=FAKE, w
                                   eps, ws, wsb, None)
 
 
+def lin_w(d, q=FAKE, k=FAKE, v=FAKE, g=FAKE, w=FAKE, out=FAKE, acc=0, eps=1e-6, ws=FAKE,
+          wsb=1 << 40):
+    return hla.lib.hla_linear_write_gated_fwd(ctypes.byref(d) if d is not None else None, q, k, v,
+                                              g, w, out, acc, eps, ws, wsb, None)
+
+
 def sm(d, q=FAKE, k=FAKE, v=FAKE, g=FAKE, out=FAKE, acc=0, scale=0.1, ws=FAKE, wsb=1 << 40):
     return hla.lib.hla_softmax_anchor_fwd(ctypes.byref(d) if d is not None else None, q, k, v, g,
                                           out, acc, scale, ws, wsb, None)
@@ -67,7 +73,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert hla.hla_abi_version() == 2
+    assert hla.hla_abi_version() == 3
     for code, name in hla.STATUS.items():
         assert hla.hla_status_str(code) == name
     assert hla.hla_status_str(99) == "HLA_UNKNOWN"
@@ -88,9 +94,9 @@ def test_workspace_bytes_pure_and_sized():
     assert hla.lib.hla_linear_workspace_bytes(None) == 0
 
 
-@pytest.mark.parametrize("call", ["lin", "sm"])
+@pytest.mark.parametrize("call", ["lin", "lin_w", "sm"])
 def test_shape_and_dtype_errors(call):
-    f = lin if call == "lin" else sm
+    f = {"lin": lin, "lin_w": lin_w, "sm": sm}[call]
     assert f(None) == NULLP
     assert f(dims(B=-1)) == SHAPE
     assert f(dims(N=-5)) == SHAPE
@@ -119,6 +125,19 @@ def test_linear_argument_errors():
         assert lin(d, eps=eps) == BADARG
     assert lin(d, acc=2) == BADARG
     assert lin(d, acc=-1) == BADARG
+
+
+def test_write_gated_argument_errors():
+    d = dims()
+    for p in ("q", "k", "v", "g", "w", "out"):
+        assert lin_w(d, **{p: None}) == NULLP, p
+        assert lin_w(d, **{p: ODD}) == ALIGN, p
+    assert lin_w(d, ws=None) == NULLP
+    assert lin_w(d, wsb=hla.hla_linear_workspace_bytes(d) - 1) == WS
+    assert lin_w(d, eps=float("nan")) == BADARG
+    assert lin_w(d, acc=5) == BADARG
+    # empty: no-op, pointers may be NULL
+    assert lin_w(dims(N=0), q=None, k=None, v=None, g=None, w=None, out=None, ws=None, wsb=0) == OK
 
 
 def test_softmax_argument_errors():

@@ -312,3 +312,71 @@ def test_hybrid_stack_bf16_residual_and_d64():
             assert float((delta - torch.from_numpy(ref).float()).abs().max()) <= bound
         else:
             assert rel_err(delta, ref) <= TOL[torch.bfloat16]
+
+
+# ----------------------------------------------------------------------------
+# write-gated linear attention
+# ----------------------------------------------------------------------------
+
+def run_linear_w(q, k, v, g, w, eps=1e-6, out_dtype=None, accumulate=False, out=None):
+    qd, kd, vd, gd, wd = (t.contiguous().to(DEV) for t in (q, k, v, g, w))
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=DEV)
+    hla.hla_linear_write_gated_fwd(qd, kd, vd, gd, wd, out=out, accumulate=accumulate, eps=eps)
+    torch.cuda.synchronize()
+    return out
+
+
+def wlogits(shape, seed, dtype):
+    return (custom(shape, seed, torch.float32, n=1)[0] * 2.0).to(dtype)
+
+
+@pytest.mark.parametrize("D", [128, 64])
+@pytest.mark.parametrize("N", [1, 63, 64, 65, 257, 1000])
+def test_write_gated_bf16_tails(N, D):
+    q, k, v, g = make((2, 3, N, D), 8000 + N, torch.bfloat16)
+    w = wlogits((2, 3, N), 8100 + N, torch.bfloat16)
+    got = run_linear_w(q, k, v, g, w)
+    assert rel_err(got, oracle.gated_linear_write(q, k, v, g, w, 1e-6)) <= TOL[torch.bfloat16]
+
+
+@pytest.mark.parametrize("D", [32, 128])
+def test_write_gated_fp32(D):
+    q, k, v, g = make((1, 2, 300, D), 8200 + D, torch.float32)
+    w = wlogits((1, 2, 300), 8300 + D, torch.float32)
+    got = run_linear_w(q, k, v, g, w)
+    assert rel_err(got, oracle.gated_linear_write(q, k, v, g, w, 1e-6)) <= TOL[torch.float32]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_write_gate_open_equals_plain_and_closed_removes(dtype):
+    # W = +inf: bitwise the plain operator; W = -inf on every other token: the
+    # plain operator on the remaining keys and values
+    q, k, v, g = make((1, 2, 500, 128), 8400, dtype)
+    plain = run_linear(q, k, v, g)
+    opened = run_linear_w(q, k, v, g, torch.full((1, 2, 500), float("inf"), dtype=dtype))
+    assert torch.equal(plain, opened)
+    keep = torch.arange(500) % 2 == 0
+    w = torch.where(keep, float("inf"), float("-inf")).to(dtype)[None, None].expand(1, 2, 500).contiguous()
+    got = run_linear_w(q, k, v, g, w)
+    ref = oracle.gated_linear_write(q, k, v, g, w, 1e-6)
+    assert rel_err(got, ref) <= TOL[dtype]
+
+
+def test_write_gated_accumulate_fp32():
+    q, k, v, g = make((1, 2, 700, 128), 8500, torch.bfloat16)
+    w = wlogits((1, 2, 700), 8600, torch.bfloat16)
+    base = custom((1, 2, 700, 128), 8700, torch.float32, n=1)[0]
+    acc = base.to(DEV)
+    run_linear_w(q, k, v, g, w, accumulate=True, out=acc)
+    assert rel_err(acc.cpu() - base, oracle.gated_linear_write(q, k, v, g, w, 1e-6)) <= TOL[torch.bfloat16]
+
+
+def test_write_gated_full_720p():
+    w_ = BY_NAME["720p_81f"]
+    q, k, v, g = layer_inputs(w_, 0)
+    w = wlogits((w_.B, w_.H, w_.N), 8800, torch.bfloat16)
+    got = run_linear_w(q, k, v, g, w, w_.eps)
+    e = rel_err(got, oracle.gated_linear_write(q, k, v, g, w, w_.eps))
+    print(f"[720p_81f write-gated] err {e:.3e}", flush=True)
+    assert e <= TOL[torch.bfloat16]

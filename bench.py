@@ -260,6 +260,7 @@ def main():
 
     if not args.no_stack:
         details["stack"] = stack_timing(torch, hla)
+        details["other_workloads"] = [pair_timing(torch, hla, BY_NAME[n]) for n in ("480p_81f", "long_720p_193f")]
 
     line = {
         "metric": METRIC, "value": tokens / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
@@ -315,6 +316,31 @@ def duration_sweep(torch, hla):
         print(json.dumps(res), flush=True)
         del q, k, v, g, out, ws_l, ws_a
         torch.cuda.empty_cache()
+
+
+def pair_timing(torch, hla, w, reps: int = 5):
+    """One gated linear and one gated softmax layer of workload ``w`` (bf16)."""
+    q, k, v, g = gpu_inputs(w, 0, torch)
+    ws_l, ws_a = hla.linear_workspace(q), hla.anchor_workspace(q)
+    out = torch.empty_like(q)
+    res = {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D}
+    for name, fn in (("linear", lambda: hla.hla_linear_fwd(q, k, v, g, out=out, eps=w.eps, workspace=ws_l)),
+                     ("softmax", lambda: hla.hla_softmax_anchor_fwd(q, k, v, g, out=out, scale=w.scale,
+                                                                    workspace=ws_a))):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        res[f"{name}_ms"] = round(a.elapsed_time(b) / reps, 4)
+    BH, N, D = w.B * w.H, w.N, w.D
+    res["linear_frac_hbm_peak"] = round(10.0 * N * D * BH / (res["linear_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+    res["softmax_frac_mfma_peak"] = round(4.0 * N * N * D * BH / (res["softmax_ms"] * 1e-3) / 1e12
+                                          / PEAK_BF16_TFLOPS, 4)
+    return res
 
 
 def stack_timing(torch, hla):

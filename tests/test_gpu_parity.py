@@ -380,3 +380,35 @@ def test_write_gated_full_720p():
     e = rel_err(got, oracle.gated_linear_write(q, k, v, g, w, w_.eps))
     print(f"[720p_81f write-gated] err {e:.3e}", flush=True)
     assert e <= TOL[torch.bfloat16]
+
+
+def test_graph_capture_replays_match_eager():
+    # the calls enqueue kernels only (no allocation, no memset), so they can be
+    # captured in a HIP graph; every replay must reproduce the eager result
+    B, H, N, D = 1, 4, 1500, 128
+    q, k, v, g = (t.to(DEV) for t in make((B, H, N, D), 9000, torch.bfloat16))
+    w = wlogits((B, H, N), 9100, torch.bfloat16).to(DEV)
+    ws_l, ws_a = hla.linear_workspace(q), hla.anchor_workspace(q)
+    out_l, out_a, out_w = (torch.empty_like(q) for _ in range(3))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        hla.hla_linear_fwd(q, k, v, g, out=out_l, workspace=ws_l)
+        hla.hla_softmax_anchor_fwd(q, k, v, g, out=out_a, workspace=ws_a)
+        hla.hla_linear_write_gated_fwd(q, k, v, g, w, out=out_w, workspace=ws_l)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (out_l, out_a, out_w)]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        hla.hla_linear_fwd(q, k, v, g, out=out_l, workspace=ws_l)
+        hla.hla_softmax_anchor_fwd(q, k, v, g, out=out_a, workspace=ws_a)
+        hla.hla_linear_write_gated_fwd(q, k, v, g, w, out=out_w, workspace=ws_l)
+    for rep in range(3):
+        for t in (out_l, out_a, out_w):
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, ref in zip((out_l, out_a, out_w), eager):
+            assert torch.equal(got, ref), rep

@@ -9,8 +9,9 @@ describe (480x832 video at 81/121/193 frames, "about 19,000 tokens" at 720p; pag
 "SANA-Video 2.0 ... (ai-papers.net)", sections on hybrid linear attention and on
 experimental results). The pages publish no tensors, so every value here is
 i.i.d. N(0, 1) from a seeded CPU generator, rounded to bf16 (round to nearest even)
-for the bf16 workloads. The same rounded tensors go to the GPU and, upcast
-exactly, to the oracle.
+for the bf16 workloads, or to OCP fp8 e4m3 for fp8 inputs (torch's cast; N(0, 1)
+draws stay far inside its +-448 range). The same rounded tensors go to the GPU and,
+upcast exactly, to the oracle.
 """
 from __future__ import annotations
 
@@ -37,7 +38,7 @@ class Workload:
     H: int
     N: int
     D: int
-    dtype: str          # "f32" or "bf16"
+    dtype: str          # "f32", "bf16" or "fp8"
     latent: Tuple[int, int, int]  # (T, H, W) latent grid; N = T*H*W
     kinds: Tuple[int, ...] = (LINEAR, SOFTMAX)
     eps: float = 1e-6
@@ -45,7 +46,7 @@ class Workload:
 
     @property
     def torch_dtype(self) -> torch.dtype:
-        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+        return {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}[self.dtype]
 
     @property
     def scale(self) -> float:
@@ -102,16 +103,19 @@ def randn(shape, seed: int, dtype: torch.dtype) -> torch.Tensor:
     return t if dtype == torch.float32 else t.to(dtype)
 
 
-def layer_inputs(w: Workload, layer: int, B: int = None, H: int = None, N: int = None):
+def layer_inputs(w: Workload, layer: int, B: int = None, H: int = None, N: int = None,
+                 dtype: torch.dtype = None):
     """(q, k, v, g) CPU tensors of shape [B, H, N, D] for ``layer`` of workload ``w``.
 
-    B/H/N may be overridden (smaller shapes for tests) while keeping the seeds.
+    B/H/N may be overridden (smaller shapes for tests) while keeping the seeds;
+    ``dtype`` overrides the workload's (e.g. fp8 inputs of a bf16 workload).
     """
     B = w.B if B is None else B
     H = w.H if H is None else H
     N = w.N if N is None else N
+    dt = w.torch_dtype if dtype is None else dtype
     shape = (B, H, N, w.D)
-    return tuple(randn(shape, seed_for(w.index, layer, s), w.torch_dtype) for s in ("q", "k", "v", "g"))
+    return tuple(randn(shape, seed_for(w.index, layer, s), dt) for s in ("q", "k", "v", "g"))
 
 
 def residual_x0(w: Workload, B: int = None, H: int = None, N: int = None) -> torch.Tensor:

@@ -23,10 +23,16 @@
  * returns. Pointer arrays and `kinds` of the stack call are HOST arrays.
  *
  * Supported combinations:
- *   in_dtype HLA_F32  -> out_dtype HLA_F32                 D in {32, 64, 128}
- *   in_dtype HLA_BF16 -> out_dtype HLA_BF16 or HLA_F32     D in {64, 128}
+ *   in_dtype HLA_F32      -> out_dtype HLA_F32                 D in {32, 64, 128}
+ *   in_dtype HLA_BF16     -> out_dtype HLA_BF16 or HLA_F32     D in {64, 128}
+ *   in_dtype HLA_FP8_E4M3 -> out_dtype HLA_BF16 or HLA_F32     D in {64, 128},
+ *                            linear calls only (softmax and a stack with a softmax
+ *                            layer return HLA_ERR_UNSUPPORTED)
  * bf16 paths multiply in bf16 on the matrix cores and accumulate in fp32; the fp32
- * paths compute in fp32 throughout.
+ * paths compute in fp32 throughout. fp8 inputs (OCP e4m3: 1 sign, 4 exponent, 3
+ * mantissa bits, bias 7, no infinities) take one byte per element and are converted
+ * exactly to bf16 where the kernels read them, so results are those of the bf16
+ * path on the same values at half the input bytes.
  *
  * Errors: every argument is checked on the host before any HIP call. On error
  * nothing is enqueued and the output is untouched. On success the work is
@@ -49,9 +55,9 @@
 extern "C" {
 #endif
 
-#define HLA_ABI_VERSION 3
+#define HLA_ABI_VERSION 4
 
-typedef enum { HLA_F32 = 0, HLA_BF16 = 1 } hla_dtype;
+typedef enum { HLA_F32 = 0, HLA_BF16 = 1, HLA_FP8_E4M3 = 2 } hla_dtype;
 
 typedef enum { HLA_LAYER_LINEAR = 0, HLA_LAYER_SOFTMAX = 1 } hla_layer_kind;
 

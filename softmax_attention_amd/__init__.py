@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(HERE, "libhla.so")
 
 HLA_F32 = 0
 HLA_BF16 = 1
+HLA_FP8_E4M3 = 2
 HLA_LAYER_LINEAR = 0
 HLA_LAYER_SOFTMAX = 1
 STATUS = {
@@ -120,6 +121,8 @@ def _dtype_code(dt) -> int:
         return HLA_F32
     if dt == torch.bfloat16:
         return HLA_BF16
+    if dt == torch.float8_e4m3fn:
+        return HLA_FP8_E4M3
     raise TypeError(f"unsupported dtype {dt}")
 
 
@@ -131,6 +134,12 @@ def dims_of(q, out_dtype=None) -> hla_dims:
     ind = _dtype_code(q)
     outd = ind if out_dtype is None else _dtype_code(out_dtype)
     return hla_dims(B, H, N, D, ind, outd)
+
+
+def _new_out(q):
+    """Default output: q's dtype, except bf16 for fp8 inputs (fp8 outputs are not built)."""
+    torch = _torch()
+    return torch.empty_like(q, dtype=torch.bfloat16 if q.dtype == torch.float8_e4m3fn else None)
 
 
 def _check(*ts):
@@ -198,7 +207,7 @@ def hla_linear_fwd(q, k, v, g, out=None, accumulate: bool = False, eps: float = 
     torch = _torch()
     _check(q, k, v, g)
     if out is None:
-        out = torch.empty_like(q)
+        out = _new_out(q)
     _check(q, out)
     d = dims_of(q, out.dtype)
     if workspace is None:
@@ -222,7 +231,7 @@ def hla_linear_write_gated_fwd(q, k, v, g, w, out=None, accumulate: bool = False
     if not w.is_cuda:
         raise ValueError("tensors must live on the GPU")
     if out is None:
-        out = torch.empty_like(q)
+        out = _new_out(q)
     _check(q, out)
     d = dims_of(q, out.dtype)
     if workspace is None:
@@ -242,7 +251,7 @@ def hla_softmax_anchor_fwd(q, k, v, g, out=None, accumulate: bool = False,
     torch = _torch()
     _check(q, k, v, g)
     if out is None:
-        out = torch.empty_like(q)
+        out = _new_out(q)
     _check(q, out)
     d = dims_of(q, out.dtype)
     scale = 1.0 / math.sqrt(q.shape[-1]) if scale is None else float(scale)

@@ -27,15 +27,14 @@ namespace {
 
 constexpr int64_t kMaxIndex = 0x7fffffffLL;  // per-head offsets are 32-bit in places
 
-bool dtype_ok(int32_t x) { return x == HLA_F32 || x == HLA_BF16; }
-
-size_t elem_bytes(int32_t dt) { return dt == HLA_F32 ? 4 : 2; }
+bool in_dtype_ok(int32_t x) { return x == HLA_F32 || x == HLA_BF16 || x == HLA_FP8_E4M3; }
+bool out_dtype_ok(int32_t x) { return x == HLA_F32 || x == HLA_BF16; }
 
 // Shape and dtype checks shared by all entry points.
 hla_status check_dims(const hla_dims* d) {
   if (!d) return HLA_ERR_NULL_PTR;
   if (d->B < 0 || d->H < 0 || d->N < 0 || d->D <= 0) return HLA_ERR_BAD_SHAPE;
-  if (!dtype_ok(d->in_dtype) || !dtype_ok(d->out_dtype)) return HLA_ERR_UNSUPPORTED;
+  if (!in_dtype_ok(d->in_dtype) || !out_dtype_ok(d->out_dtype)) return HLA_ERR_UNSUPPORTED;
   if (d->in_dtype == HLA_F32) {
     if (d->out_dtype != HLA_F32) return HLA_ERR_UNSUPPORTED;
     if (d->D != 32 && d->D != 64 && d->D != 128) return HLA_ERR_UNSUPPORTED;
@@ -94,7 +93,7 @@ LinearPlan linear_plan(const hla_dims& d) {
   P = P < 1 ? 1 : (P > max_p ? max_p : P);
   p.P = int(P);
   const size_t part = size_t(BH) * size_t(c) * size_t(D * D + D) * 4;
-  if (d.in_dtype == HLA_BF16)
+  if (d.in_dtype != HLA_F32)
     p.state_bytes = size_t((D / 16 + 1) * (D / 32)) * 1024;  // MFMA operand fragments
   else
     p.state_bytes = size_t(D * D + D) * 4;                   // fp32 S and z
@@ -128,7 +127,7 @@ static hla_status linear_common(const hla_dims* d, const void* q, const void* k,
   if (workspace_bytes < plan.total) return HLA_ERR_WORKSPACE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   clear_pending_error();
-  if (d->in_dtype == HLA_BF16)
+  if (d->in_dtype != HLA_F32)  // bf16, or fp8 converted to bf16 on load
     return from_hip(launch_linear_bf16(*d, q, k, v, g, w, out, accumulate, eps, workspace, plan, s));
   return from_hip(launch_linear_f32(*d, q, k, v, g, w, out, accumulate, eps, workspace, plan, s));
 }
@@ -183,6 +182,7 @@ hla_status hla_softmax_anchor_fwd(const hla_dims* d, const void* q, const void* 
   if (st != HLA_OK) return st;
   if (!isfinite(scale) || scale <= 0.f || (accumulate != 0 && accumulate != 1))
     return HLA_ERR_BAD_ARG;
+  if (d->in_dtype == HLA_FP8_E4M3) return HLA_ERR_UNSUPPORTED;
   if (empty(d)) return HLA_OK;
   if ((st = check_tensors(q, k, v, g, out)) != HLA_OK) return st;
   const size_t need = anchor_workspace_bytes(*d);
@@ -214,6 +214,7 @@ hla_status hla_hybrid_stack_fwd(const hla_dims* d, int n_layers, const int32_t* 
     any_linear |= kinds[l] == HLA_LAYER_LINEAR;
     any_softmax |= kinds[l] == HLA_LAYER_SOFTMAX;
   }
+  if (any_softmax && d->in_dtype == HLA_FP8_E4M3) return HLA_ERR_UNSUPPORTED;
   if (empty(d)) return HLA_OK;
   for (int l = 0; l < n_layers; ++l)
     if ((st = check_tensors(q[l], k[l], v[l], g[l], x)) != HLA_OK) return st;
@@ -230,7 +231,7 @@ hla_status hla_hybrid_stack_fwd(const hla_dims* d, int n_layers, const int32_t* 
     if (workspace_bytes < need) return HLA_ERR_WORKSPACE;
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const bool bf = d->in_dtype == HLA_BF16;
+  const bool bf = d->in_dtype != HLA_F32;  // bf16, or fp8 (linear layers only)
   clear_pending_error();
   for (int l = 0; l < n_layers; ++l) {
     hipError_t e;

@@ -129,4 +129,46 @@ __device__ __forceinline__ u32x4 ldg16_stream(const void* p) {
 }
 __device__ __forceinline__ void stg16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
+// ---- fp8 (OCP e4m3) inputs ---------------------------------------------------
+// Every e4m3 value is exactly representable in bf16 (4-bit exponent, 3-bit
+// mantissa), so fp8 inputs convert losslessly into the bf16 operands the
+// kernels already use.
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+
+// four fp8 bytes -> four floats (bytes 0,1 then 2,3), exact
+__device__ __forceinline__ f32x4 fp8x4_to_f32(uint32_t w) {
+  const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+  const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+  return (f32x4){lo[0], lo[1], hi[0], hi[1]};
+}
+__device__ __forceinline__ float fp8_to_f32(uint8_t b) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8((uint32_t)b, false)[0];
+}
+// eight fp8 values (8 bytes) -> eight bf16 (one 16-byte MFMA operand), exact
+__device__ __forceinline__ u32x4 fp8x8_to_bf16(u32x2 w) {
+  const f32x4 a = fp8x4_to_f32(w[0]), b = fp8x4_to_f32(w[1]);
+  return (u32x4){pack_bf16(a[0], a[1]), pack_bf16(a[2], a[3]), pack_bf16(b[0], b[1]),
+                 pack_bf16(b[2], b[3])};
+}
+
+// Eight consecutive elements of a bf16 or fp8 tensor as eight bf16 values.
+template <typename T>
+__device__ __forceinline__ u32x4 load8_bf16(const T* p) {
+  if constexpr (sizeof(T) == 1) return fp8x8_to_bf16(*reinterpret_cast<const u32x2*>(p));
+  else return *reinterpret_cast<const u32x4*>(p);
+}
+// Same, with a non-temporal (streaming) load.
+template <typename T>
+__device__ __forceinline__ u32x4 load8_bf16_stream(const T* p) {
+  if constexpr (sizeof(T) == 1)
+    return fp8x8_to_bf16(__builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p)));
+  else return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+// One element of a bf16 or fp8 tensor as float.
+template <typename T>
+__device__ __forceinline__ float elem_f32(T x) {
+  if constexpr (sizeof(T) == 1) return fp8_to_f32(x);
+  else return bf16_to_f32(x);
+}
+
 }  // namespace hla

@@ -32,10 +32,12 @@ constexpr int kTile = 64;  // tokens per LDS tile in the state pass
 // With WG (the write-gated variant) each token's phi(K) row is first scaled by
 // its write strength sigma(W_n), W one bf16 logit per token and head ([B,H,N]);
 // the scaled row, rounded to bf16, feeds both the MFMA and the normaliser sum.
-template <int D, bool WG>
-__global__ __launch_bounds__(256) void linear_state_bf16(const uint16_t* __restrict__ K,
-                                                         const uint16_t* __restrict__ V,
-                                                         const uint16_t* __restrict__ W,
+// TIn: uint16_t for bf16 inputs, uint8_t for fp8 (e4m3) inputs, converted
+// exactly to bf16 as they are loaded.
+template <int D, bool WG, typename TIn>
+__global__ __launch_bounds__(256) void linear_state_bf16(const TIn* __restrict__ K,
+                                                         const TIn* __restrict__ V,
+                                                         const TIn* __restrict__ W,
                                                          float* __restrict__ part, int N, int T,
                                                          int C) {
   constexpr int CH = D / 8;                // 16-byte chunks per token row
@@ -50,12 +52,12 @@ __global__ __launch_bounds__(256) void linear_state_bf16(const uint16_t* __restr
   const int n0 = c * T;
   const int n1 = min(N, n0 + T);
   const size_t base = (size_t)bh * N * D;
-  const uint16_t* Kh = K + base;
-  const uint16_t* Vh = V + base;
+  const TIn* Kh = K + base;
+  const TIn* Vh = V + base;
 
   u32x4 kr[LOADS], vr[LOADS];
-  uint16_t wr[LOADS];
-  const uint16_t* Wh = WG ? W + (size_t)bh * N : nullptr;
+  TIn wr[LOADS];
+  const TIn* Wh = WG ? W + (size_t)bh * N : nullptr;
   float zacc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) zacc[e] = 0.f;
@@ -71,8 +73,8 @@ __global__ __launch_bounds__(256) void linear_state_bf16(const uint16_t* __restr
       const int chunk = tid + 256 * i;
       const int n = t0 + chunk / CH, col = (chunk % CH) * 8;
       if (n < n1) {
-        kr[i] = ldg16_stream(Kh + (size_t)n * D + col);
-        vr[i] = ldg16_stream(Vh + (size_t)n * D + col);
+        kr[i] = load8_bf16_stream(Kh + (size_t)n * D + col);
+        vr[i] = load8_bf16_stream(Vh + (size_t)n * D + col);
         if (WG) wr[i] = Wh[n];
       } else {
         kr[i] = (u32x4){0, 0, 0, 0};
@@ -95,7 +97,7 @@ __global__ __launch_bounds__(256) void linear_state_bf16(const uint16_t* __restr
       const int row = chunk / CH, col = (chunk % CH) * 8;
       u32x4 kk = relu_bf16x8(kr[i]);
       if (WG) {
-        const float beta = sigmoid(bf16_to_f32(wr[i]));
+        const float beta = sigmoid(elem_f32(wr[i]));
 #pragma unroll
         for (int p = 0; p < 4; ++p) kk[p] = pack_bf16(bf_lo(kk[p]) * beta, bf_hi(kk[p]) * beta);
       }
@@ -241,9 +243,9 @@ __global__ __launch_bounds__(256) void linear_reduce_bf16(const float* __restric
 // its B-operand slice for k-step t and, by the fragment row order above, the
 // feature slice of its output values -- so Q, G and O each move as 16-byte
 // accesses with no shuffles.
-template <int D, bool OUT_F32>
-__global__ __launch_bounds__(256, 2) void linear_out_bf16(const uint16_t* __restrict__ Q,
-                                                       const uint16_t* __restrict__ G,
+template <int D, bool OUT_F32, typename TIn>
+__global__ __launch_bounds__(256, 2) void linear_out_bf16(const TIn* __restrict__ Q,
+                                                       const TIn* __restrict__ G,
                                                        void* __restrict__ out,
                                                        const uint32_t* __restrict__ state, int N,
                                                        float eps, int accumulate) {
@@ -260,8 +262,8 @@ __global__ __launch_bounds__(256, 2) void linear_out_bf16(const uint16_t* __rest
 
   const int n = lane & 15, g = lane >> 4;
   const size_t base = (size_t)bh * N * D;
-  const uint16_t* Qh = Q + base;
-  const uint16_t* Gh = G + base;
+  const TIn* Qh = Q + base;
+  const TIn* Gh = G + base;
   const int stride = gridDim.x * 4;
   int grp = blockIdx.x * 4 + wave;
   if (grp * 16 >= N) return;
@@ -272,8 +274,8 @@ __global__ __launch_bounds__(256, 2) void linear_out_bf16(const uint16_t* __rest
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       if (tok < N) {
-        qd[t] = ldg16(Qh + (size_t)tok * D + 32 * t + 8 * g);
-        gd[t] = ldg16(Gh + (size_t)tok * D + 32 * t + 8 * g);
+        qd[t] = load8_bf16(Qh + (size_t)tok * D + 32 * t + 8 * g);
+        gd[t] = load8_bf16(Gh + (size_t)tok * D + 32 * t + 8 * g);
       } else {
         qd[t] = (u32x4){0, 0, 0, 0};
         gd[t] = (u32x4){0, 0, 0, 0};
@@ -356,7 +358,7 @@ __global__ __launch_bounds__(256, 2) void linear_out_bf16(const uint16_t* __rest
   }
 }
 
-template <int D>
+template <int D, typename TIn>
 hipError_t launch_d(const hla_dims& d, const void* q, const void* k, const void* v, const void* g,
                     const void* w, void* out, int accumulate, float eps, void* ws,
                     const LinearPlan& plan, hipStream_t stream) {
@@ -364,24 +366,24 @@ hipError_t launch_d(const hla_dims& d, const void* q, const void* k, const void*
   char* wsb = reinterpret_cast<char*>(ws);
   float* part = reinterpret_cast<float*>(wsb + plan.part_off);
   uint32_t* state = reinterpret_cast<uint32_t*>(wsb + plan.state_off);
+  const TIn* Kp = reinterpret_cast<const TIn*>(k);
+  const TIn* Vp = reinterpret_cast<const TIn*>(v);
+  const TIn* Qp = reinterpret_cast<const TIn*>(q);
+  const TIn* Gp = reinterpret_cast<const TIn*>(g);
   if (w)
-    hipLaunchKernelGGL((linear_state_bf16<D, true>), dim3(plan.C, BH), dim3(256), 0, stream,
-                       reinterpret_cast<const uint16_t*>(k), reinterpret_cast<const uint16_t*>(v),
-                       reinterpret_cast<const uint16_t*>(w), part, N, plan.T, plan.C);
+    hipLaunchKernelGGL((linear_state_bf16<D, true, TIn>), dim3(plan.C, BH), dim3(256), 0, stream,
+                       Kp, Vp, reinterpret_cast<const TIn*>(w), part, N, plan.T, plan.C);
   else
-    hipLaunchKernelGGL((linear_state_bf16<D, false>), dim3(plan.C, BH), dim3(256), 0, stream,
-                       reinterpret_cast<const uint16_t*>(k), reinterpret_cast<const uint16_t*>(v),
-                       nullptr, part, N, plan.T, plan.C);
+    hipLaunchKernelGGL((linear_state_bf16<D, false, TIn>), dim3(plan.C, BH), dim3(256), 0, stream,
+                       Kp, Vp, nullptr, part, N, plan.T, plan.C);
   hipLaunchKernelGGL(linear_reduce_bf16<D>, dim3(D * D / 8 / 256 + 1, BH), dim3(256), 0, stream,
                      part, state, plan.C);
   if (d.out_dtype == HLA_F32)
-    hipLaunchKernelGGL((linear_out_bf16<D, true>), dim3(plan.P, BH), dim3(256), 0, stream,
-                       reinterpret_cast<const uint16_t*>(q), reinterpret_cast<const uint16_t*>(g),
-                       out, state, N, eps, accumulate);
+    hipLaunchKernelGGL((linear_out_bf16<D, true, TIn>), dim3(plan.P, BH), dim3(256), 0, stream,
+                       Qp, Gp, out, state, N, eps, accumulate);
   else
-    hipLaunchKernelGGL((linear_out_bf16<D, false>), dim3(plan.P, BH), dim3(256), 0, stream,
-                       reinterpret_cast<const uint16_t*>(q), reinterpret_cast<const uint16_t*>(g),
-                       out, state, N, eps, accumulate);
+    hipLaunchKernelGGL((linear_out_bf16<D, false, TIn>), dim3(plan.P, BH), dim3(256), 0, stream,
+                       Qp, Gp, out, state, N, eps, accumulate);
   return hipGetLastError();
 }
 
@@ -390,8 +392,14 @@ hipError_t launch_d(const hla_dims& d, const void* q, const void* k, const void*
 hipError_t launch_linear_bf16(const hla_dims& d, const void* q, const void* k, const void* v,
                               const void* g, const void* w, void* out, int accumulate, float eps,
                               void* ws, const LinearPlan& plan, hipStream_t stream) {
-  if (d.D == 128) return launch_d<128>(d, q, k, v, g, w, out, accumulate, eps, ws, plan, stream);
-  return launch_d<64>(d, q, k, v, g, w, out, accumulate, eps, ws, plan, stream);
+  if (d.in_dtype == HLA_FP8_E4M3) {
+    if (d.D == 128)
+      return launch_d<128, uint8_t>(d, q, k, v, g, w, out, accumulate, eps, ws, plan, stream);
+    return launch_d<64, uint8_t>(d, q, k, v, g, w, out, accumulate, eps, ws, plan, stream);
+  }
+  if (d.D == 128)
+    return launch_d<128, uint16_t>(d, q, k, v, g, w, out, accumulate, eps, ws, plan, stream);
+  return launch_d<64, uint16_t>(d, q, k, v, g, w, out, accumulate, eps, ws, plan, stream);
 }
 
 }  // namespace hla

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "hla.h")
 
 OK, NULLP, SHAPE, UNSUP, BADARG, ALIGN, WS, HIP = range(8)
-F32, BF16 = hla.HLA_F32, hla.HLA_BF16
+F32, BF16, FP8 = hla.HLA_F32, hla.HLA_BF16, hla.HLA_FP8_E4M3
 FAKE = 0x10000  # a 16-byte-aligned address that is never dereferenced
 ODD = 0x10008   # 8-byte aligned only
 
@@ -73,7 +73,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert hla.hla_abi_version() == 3
+    assert hla.hla_abi_version() == 4
     for code, name in hla.STATUS.items():
         assert hla.hla_status_str(code) == name
     assert hla.hla_status_str(99) == "HLA_UNKNOWN"
@@ -106,7 +106,9 @@ def test_shape_and_dtype_errors(call):
     assert f(dims(D=32)) == UNSUP                  # bf16 path built for D in {64, 128}
     assert f(dims(i=F32, o=BF16, D=32)) == UNSUP   # fp32 in -> bf16 out not built
     assert f(dims(i=7)) == UNSUP
-    assert f(dims(o=2)) == UNSUP
+    assert f(dims(o=FP8)) == UNSUP                 # fp8 outputs are not built
+    assert f(dims(i=FP8, o=FP8)) == UNSUP
+    assert f(dims(i=FP8, D=32)) == UNSUP
     assert f(dims(N=1 << 31)) == SHAPE             # N*D overflows 32-bit offsets
     assert f(dims(B=1 << 40)) == SHAPE
 
@@ -138,6 +140,20 @@ def test_write_gated_argument_errors():
     assert lin_w(d, acc=5) == BADARG
     # empty: no-op, pointers may be NULL
     assert lin_w(dims(N=0), q=None, k=None, v=None, g=None, w=None, out=None, ws=None, wsb=0) == OK
+
+
+def test_fp8_inputs():
+    # fp8 inputs are built for the linear calls; they take the bf16 path's
+    # workspace (the state is formed from the same values)
+    for o in (BF16, F32):
+        for D in (64, 128):
+            assert hla.hla_linear_workspace_bytes(dims(D=D, i=FP8, o=o)) == \
+                hla.hla_linear_workspace_bytes(dims(D=D, i=BF16, o=o))
+    d = dims(i=FP8, o=BF16)
+    assert lin(d, q=ODD) == ALIGN
+    assert lin_w(d, w=None) == NULLP
+    assert lin(d, wsb=hla.hla_linear_workspace_bytes(d) - 1) == WS
+    assert stack(dims(i=FP8, o=F32), kinds=(0, 0), ws=None) == NULLP
 
 
 def test_softmax_argument_errors():
@@ -223,6 +239,8 @@ def test_binding_dims():
     d = hla.dims_of(t)
     assert d.out_dtype == BF16
     assert hla.dims_of(t.float(), t.float()).in_dtype == F32
+    d = hla.dims_of(t.to(torch.float8_e4m3fn), torch.bfloat16)
+    assert (d.in_dtype, d.out_dtype) == (FP8, BF16)
     with pytest.raises(TypeError):
         hla.dims_of(t.half())
 

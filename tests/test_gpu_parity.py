@@ -2,6 +2,8 @@
 
 Tolerances (metric: max |gpu - ref| / max |ref| per [b, h] slab, worst slab):
   bf16 inputs, fp32 accumulation : 2e-2
+  fp8 inputs (converted exactly to bf16 in the kernels): 2e-2, against the
+                                   oracle on the same fp8 values
   fp32 path                      : 1e-4
 Any NaN/Inf fails. Small shapes span several tiles and ragged tails; the full
 workload sizes run in the same launch configuration the benchmark times, with
@@ -22,6 +24,11 @@ pytestmark = pytest.mark.gpu
 
 TOL = {torch.bfloat16: 2e-2, torch.float32: 1e-4}
 DEV = "cuda"
+FP8 = torch.float8_e4m3fn
+
+
+def out_dtype_for(dtype):
+    return torch.bfloat16 if dtype == FP8 else dtype
 
 
 def rel_err(got, ref):
@@ -35,7 +42,7 @@ def make(shape, seed, dtype):
 def run_linear(q, k, v, g, eps=1e-6, out_dtype=None, accumulate=False, out=None):
     qd, kd, vd, gd = (t.contiguous().to(DEV) for t in (q, k, v, g))
     if out is None:
-        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=DEV)
+        out = torch.empty(q.shape, dtype=out_dtype or out_dtype_for(q.dtype), device=DEV)
     hla.hla_linear_fwd(qd, kd, vd, gd, out=out, accumulate=accumulate, eps=eps)
     torch.cuda.synchronize()
     return out
@@ -44,7 +51,7 @@ def run_linear(q, k, v, g, eps=1e-6, out_dtype=None, accumulate=False, out=None)
 def run_softmax(q, k, v, g, scale=None, out_dtype=None, accumulate=False, out=None):
     qd, kd, vd, gd = (t.contiguous().to(DEV) for t in (q, k, v, g))
     if out is None:
-        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=DEV)
+        out = torch.empty(q.shape, dtype=out_dtype or out_dtype_for(q.dtype), device=DEV)
     hla.hla_softmax_anchor_fwd(qd, kd, vd, gd, out=out, accumulate=accumulate, scale=scale)
     torch.cuda.synchronize()
     return out
@@ -321,7 +328,7 @@ def test_hybrid_stack_bf16_residual_and_d64():
 def run_linear_w(q, k, v, g, w, eps=1e-6, out_dtype=None, accumulate=False, out=None):
     qd, kd, vd, gd, wd = (t.contiguous().to(DEV) for t in (q, k, v, g, w))
     if out is None:
-        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=DEV)
+        out = torch.empty(q.shape, dtype=out_dtype or out_dtype_for(q.dtype), device=DEV)
     hla.hla_linear_write_gated_fwd(qd, kd, vd, gd, wd, out=out, accumulate=accumulate, eps=eps)
     torch.cuda.synchronize()
     return out
@@ -412,3 +419,72 @@ def test_graph_capture_replays_match_eager():
         torch.cuda.synchronize()
         for got, ref in zip((out_l, out_a, out_w), eager):
             assert torch.equal(got, ref), rep
+
+
+# ----------------------------------------------------------------------------
+# fp8 (OCP e4m3) inputs
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("D", [128, 64])
+@pytest.mark.parametrize("N", [1, 63, 65, 257, 1000])
+def test_linear_fp8_tails(N, D, out_dtype):
+    q, k, v, g = make((2, 2, N, D), 10000 + N + D, FP8)
+    got = run_linear(q, k, v, g, out_dtype=out_dtype)
+    assert got.dtype == out_dtype
+    assert rel_err(got, oracle.gated_linear(q, k, v, g, 1e-6)) <= TOL[torch.bfloat16]
+
+
+@pytest.mark.parametrize("gated", [False, True])
+def test_linear_fp8_equals_bf16_path_on_same_values(gated):
+    # every e4m3 value is a bf16 value and the kernels convert on load, so the
+    # fp8 call must reproduce the bf16 call on the upcast tensors bit for bit
+    q, k, v, g = make((2, 3, 1500, 128), 10100, FP8)
+    w = wlogits((2, 3, 1500), 10200, FP8)
+    up = [t.to(torch.bfloat16) for t in (q, k, v, g, w)]
+    if gated:
+        a, b = run_linear_w(q, k, v, g, w), run_linear_w(*up)
+    else:
+        a, b = run_linear(q, k, v, g), run_linear(*up[:4])
+    assert a.dtype == b.dtype == torch.bfloat16
+    assert torch.equal(a, b)
+
+
+def test_linear_fp8_binding_defaults_to_bf16_output():
+    q, k, v, g = (t.to(DEV) for t in make((1, 2, 300, 64), 10300, FP8))
+    out = hla.hla_linear_fwd(q, k, v, g)
+    torch.cuda.synchronize()
+    assert out.dtype == torch.bfloat16
+    assert rel_err(out, oracle.gated_linear(q.cpu(), k.cpu(), v.cpu(), g.cpu(), 1e-6)) <= 2e-2
+
+
+@pytest.mark.parametrize("N", [65, 1000])
+def test_write_gated_fp8(N):
+    q, k, v, g = make((2, 2, N, 128), 10400 + N, FP8)
+    w = wlogits((2, 2, N), 10500 + N, FP8)
+    got = run_linear_w(q, k, v, g, w, out_dtype=torch.float32)
+    assert rel_err(got, oracle.gated_linear_write(q, k, v, g, w, 1e-6)) <= TOL[torch.bfloat16]
+
+
+def test_linear_fp8_accumulate_and_stack():
+    # accumulate into an fp32 stream, directly and through a linear-only stack
+    B, H, N, D = 1, 2, 900, 128
+    layers = [make((B, H, N, D), 10600 + 10 * l, FP8) for l in range(3)]
+    x0 = custom((B, H, N, D), 10700, torch.float32, n=1)[0]
+    x = x0.to(DEV)
+    hla.hla_hybrid_stack_fwd(x, [tuple(t.to(DEV) for t in L) for L in layers], [0, 0, 0])
+    torch.cuda.synchronize()
+    ref = sum(oracle.gated_linear(*L, 1e-6) for L in layers)
+    assert rel_err(x.cpu() - x0, ref) <= 2e-2
+    acc = x0.to(DEV)
+    run_linear(*layers[0], accumulate=True, out=acc)
+    assert rel_err(acc.cpu() - x0, oracle.gated_linear(*layers[0], 1e-6)) <= 2e-2
+
+
+def test_linear_fp8_full_720p():
+    w = BY_NAME["720p_81f"]
+    q, k, v, g = layer_inputs(w, 0, dtype=FP8)
+    got = run_linear(q, k, v, g, w.eps)
+    e = rel_err(got, oracle.gated_linear(q, k, v, g, w.eps))
+    print(f"[720p_81f fp8] linear err {e:.3e}", flush=True)
+    assert e <= 2e-2

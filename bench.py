@@ -14,7 +14,8 @@ stack).
 
 --profile {anchor,linear,step,copy} runs just that piece a few times, for
 rocprofv3 kernel traces and counter passes (copy: a plain device copy of known
-size that calibrates FETCH_SIZE / WRITE_SIZE).
+size that calibrates FETCH_SIZE / WRITE_SIZE); anchor_fp8, linear_fp8 and
+step_fp8 do the same on fp8 (e4m3) copies of the inputs.
 """
 from __future__ import annotations
 
@@ -32,6 +33,7 @@ sys.path.insert(0, ROOT)
 METRIC = "hybrid-attn layer tokens/s at 720p (N≈19k); % HBM BW / % MFMA peak"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix, TFLOP/s
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 matrix, TFLOP/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 KERNEL_SOURCES = {
     "anchor": ["softmax_attention_amd/csrc/anchor_bf16.hip", "softmax_attention_amd/csrc/hla_device.h"],
@@ -83,7 +85,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
     ap.add_argument("--no-stack", action="store_true", help="skip the hybrid-stack detail timing")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--profile", choices=["anchor", "linear", "step", "copy"], default=None)
+    ap.add_argument("--profile", default=None,
+                    choices=["anchor", "linear", "step", "copy", "anchor_fp8", "linear_fp8", "step_fp8"])
     ap.add_argument("--iters", type=int, default=5, help="launches per --profile run")
     ap.add_argument("--sweep", action="store_true",
                     help="720p duration sweep: one gated linear and one gated softmax layer per clip "
@@ -169,9 +172,12 @@ def main():
         return
 
     sets = [gpu_inputs(w, s, torch) for s in range(2)]
-    outs = [torch.empty_like(sets[0][0]) for _ in range(2)]
-    ws = hla.linear_workspace(sets[0][0])
-    ws_a = hla.anchor_workspace(sets[0][0])
+    if args.profile and args.profile.endswith("_fp8"):
+        sets = [[t.to(torch.float8_e4m3fn) for t in s_] for s_ in sets]
+        args.profile = args.profile[:-4]
+    outs = [torch.empty(sets[0][0].shape, dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    ws = hla.linear_workspace(sets[0][0], torch.bfloat16)
+    ws_a = hla.anchor_workspace(sets[0][0], torch.bfloat16)
 
     def linear(i):
         q, k, v, g = sets[i % 2]
@@ -258,6 +264,8 @@ def main():
                                      "frac_hbm_peak": round(wg_bytes / (wg_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                                      "note": "back-to-back calls (each pays the previous call's write-back)"}
 
+    details["fp8_inputs"] = fp8_timing(torch, hla, w, sets, K, lin_ms, sm_ms)
+
     if not args.no_stack:
         details["stack"] = stack_timing(torch, hla)
         details["other_workloads"] = [pair_timing(torch, hla, BY_NAME[n]) for n in ("480p_81f", "long_720p_193f")]
@@ -316,6 +324,54 @@ def duration_sweep(torch, hla):
         print(json.dumps(res), flush=True)
         del q, k, v, g, out, ws_l, ws_a
         torch.cuda.empty_cache()
+
+
+def fp8_timing(torch, hla, w, sets, K, lin_ms_bf16, sm_ms_bf16):
+    """The timed step again on fp8 (e4m3) copies of the same inputs, bf16 out.
+
+    The anchor's Q K^T runs at the fp8 matrix rate and P V at the bf16 one; the
+    two halves have equal flops, so its peak is 2 / (1/5.0 + 1/2.5) PF.
+    """
+    f8 = [[t.to(torch.float8_e4m3fn) for t in s] for s in sets]
+    out = torch.empty(f8[0][0].shape, dtype=torch.bfloat16, device=f8[0][0].device)
+    ws_l = hla.linear_workspace(f8[0][0], torch.bfloat16)
+    ws_a = hla.anchor_workspace(f8[0][0], torch.bfloat16)
+
+    def linear(i):
+        hla.hla_linear_fwd(*f8[i % 2], out=out, eps=w.eps, workspace=ws_l)
+
+    def anchor(i):
+        hla.hla_softmax_anchor_fwd(*f8[i % 2], out=out, scale=w.scale, workspace=ws_a)
+
+    for i in range(2):
+        linear(i)
+        anchor(i)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    for i in range(K):
+        ev[i][0].record()
+        linear(i)
+        ev[i][1].record()
+        anchor(i)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    lin_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    sm_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    BH, N, D = w.B * w.H, w.N, w.D
+    lin_bytes = 6.0 * N * D * BH                  # read Q, K, V, G (1 byte), write O (bf16)
+    sm_tfs = 4.0 * N * N * D * BH / (sm_ms * 1e-3) / 1e12
+    peak_mixed = 2.0 / (1.0 / PEAK_FP8_TFLOPS + 1.0 / PEAK_BF16_TFLOPS)
+    return {
+        "inputs": "fp8 e4m3 (same draws, rounded), bf16 output",
+        "linear_ms": round(lin_ms, 4), "linear_alg_bytes": lin_bytes,
+        "linear_GB_s": round(lin_bytes / (lin_ms * 1e-3) / 1e9, 1),
+        "linear_frac_hbm_peak": round(lin_bytes / (lin_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "linear_speedup_vs_bf16": round(lin_ms_bf16 / lin_ms, 3),
+        "softmax_ms": round(sm_ms, 4), "softmax_TFLOP_s": round(sm_tfs, 1),
+        "softmax_peak_TFLOP_s": round(peak_mixed, 1),
+        "softmax_frac_peak": round(sm_tfs / peak_mixed, 4),
+        "softmax_speedup_vs_bf16": round(sm_ms_bf16 / sm_ms, 3),
+    }
 
 
 def pair_timing(torch, hla, w, reps: int = 5):

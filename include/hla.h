@@ -25,14 +25,14 @@
  * Supported combinations:
  *   in_dtype HLA_F32      -> out_dtype HLA_F32                 D in {32, 64, 128}
  *   in_dtype HLA_BF16     -> out_dtype HLA_BF16 or HLA_F32     D in {64, 128}
- *   in_dtype HLA_FP8_E4M3 -> out_dtype HLA_BF16 or HLA_F32     D in {64, 128},
- *                            linear calls only (softmax and a stack with a softmax
- *                            layer return HLA_ERR_UNSUPPORTED)
+ *   in_dtype HLA_FP8_E4M3 -> out_dtype HLA_BF16 or HLA_F32     D in {64, 128}
  * bf16 paths multiply in bf16 on the matrix cores and accumulate in fp32; the fp32
  * paths compute in fp32 throughout. fp8 inputs (OCP e4m3: 1 sign, 4 exponent, 3
- * mantissa bits, bias 7, no infinities) take one byte per element and are converted
- * exactly to bf16 where the kernels read them, so results are those of the bf16
- * path on the same values at half the input bytes.
+ * mantissa bits, bias 7, no infinities) take one byte per element. The softmax
+ * anchor forms Q K^T from them on the fp8 matrix cores (exact products, fp32
+ * sums); everywhere else they are converted exactly to bf16 where the kernels
+ * read them. Results are thus those of the bf16 path on the same values, up to
+ * the fp32 summation order of Q K^T.
  *
  * Errors: every argument is checked on the host before any HIP call. On error
  * nothing is enqueued and the output is untouched. On success the work is
@@ -118,7 +118,7 @@ hla_status hla_linear_write_gated_fwd(const hla_dims* d, const void* q, const vo
                                       size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace hla_softmax_anchor_fwd needs for `d`: on the bf16
- * path a repacked copy of V (B*H*D*ceil(N/64)*64 bf16, V transposed with zero
+ * and fp8 paths a repacked copy of V (B*H*D*ceil(N/64)*64 bf16, V transposed with zero
  * keys past N) followed by room for the partial results of up to
  * P = min(256, ceil(N/256) * B*H * ceil(N/64)) key-range pieces (P*256*(D+2)
  * fp32), used when the query blocks of an incomplete last batch of workgroups

@@ -1,4 +1,4 @@
-// Gated softmax anchor, bf16 inputs, on gfx950 matrix cores.
+// Gated softmax anchor, bf16 or fp8 (OCP e4m3) inputs, on gfx950 matrix cores.
 //
 // O = sigma(G) (.) softmax_rows(scale * Q K^T) V, non-causal: the periodic
 // gated-softmax layer of SANA-Video 2.0 that restores exact token interactions
@@ -10,7 +10,8 @@
 // 64, four buffers deep with one barrier per two tiles; the eight waves share
 // each tile, so K and V cross from L2 into LDS once per 256 queries.
 // Per tile and wave:
-//   S^T = K Q^T      32x32x16 bf16 MFMA, K from LDS, Q^T held in registers; the
+//   S^T = K Q^T      32x32x16 bf16 MFMA (32x32x64 fp8 MFMA for fp8 inputs, exact
+//                    products), K from LDS, Q^T held in registers; the
 //                    transposed product puts one query per lane (and its
 //                    partner lane ^ 32), so row max and row sum need one swap.
 //   online softmax   in log2 units with a lazily updated running max: the
@@ -19,9 +20,10 @@
 //                    result exact up to rounding.
 //   O^T += V^T P^T   P^T stays in registers (the MFMA result layout is reused as
 //                    the next B operand by permuting the key order inside each
-//                    k-step). V is repacked once per call into V^T rows (a
-//                    workspace, zero keys past N) in the key order P^T uses,
-//                    so each V^T operand is one 16-byte LDS read.
+//                    k-step). V is repacked once per call into bf16 V^T rows
+//                    (a workspace, zero keys past N; fp8 values convert
+//                    exactly) in the key order P^T uses, so each V^T operand is
+//                    one 16-byte LDS read.
 // K and V^T tiles go from HBM straight into LDS through buffer loads, which
 // return zeros past the end of the head, so the last partial tile needs no
 // predicated loads; only its scores past N are masked.
@@ -42,23 +44,18 @@ constexpr int kBC = 64;   // keys per LDS tile
 constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
 constexpr int kMaxPieces = 256;  // most key-range pieces one call splits its last batch into
 
-// LDS tiles use XOR swizzles of whole 16-byte chunks instead of padding:
-//   K   (row = key, D/8 chunks): chunk c of row k sits at c ^ (k & 15)
-//       (c ^ (k & 7) for D=64), so the 32 rows one S^T operand read touches
-//       spread over all banks;
+// LDS tiles use XOR swizzles of whole 16-byte chunks instead of padding. A
+// 16-byte LDS read serves 16 lanes per cycle from the 64 banks (16 bank groups
+// of 16 bytes), and the 16 lanes read the same logical chunk of 16 consecutive
+// rows, so the swizzle must put those on 16 distinct bank groups:
+//   K   (row = key, CH = D * element size / 16 chunks): chunk c of row k sits at
+//       c ^ k_swz<CH>(k), k_swz = (k / (16 / CH)) mod CH: rows that share bank
+//       groups (k mod 16/CH equal) get CH distinct chunk positions;
 //   V^T (row = feature, 8 chunks of 8 keys): chunk c of row d sits at
 //       c ^ vt_swz(d), which puts the 16 rows one P V operand read touches on
 //       16 distinct bank groups.
-template <int D>
-struct AnchorSwz;
-template <>
-struct AnchorSwz<128> {
-  static constexpr int kmask = 15;
-};
-template <>
-struct AnchorSwz<64> {
-  static constexpr int kmask = 7;
-};
+template <int CH>
+__device__ __forceinline__ int k_swz(int k) { return (k / (16 / CH)) & (CH - 1); }
 __device__ __forceinline__ int vt_swz(int d) { return ((d >> 1) & 3) | ((d >> 2) & 4); }
 
 // Position of key k16 (0..15) of a 16-key group in the repacked V^T rows: MFMA
@@ -71,18 +68,18 @@ __device__ __forceinline__ int vt_pos(int k16) { return 8 * ((k16 >> 2) & 1) + 4
 // V -> V^T repack (once per call): per head, V^T[d][n_pad] with the key order
 // of vt_pos inside every 16-key group and zeros for keys >= N.
 // ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void anchor_pack_vt(const uint16_t* __restrict__ V,
+template <int D, typename TIn>
+__global__ __launch_bounds__(256) void anchor_pack_vt(const TIn* __restrict__ V,
                                                       uint16_t* __restrict__ VT, int N,
                                                       int n_pad) {
   constexpr int CH = D / 8;
   __shared__ uint32_t tile[64][D / 2 + 1];  // 64 keys x D features, odd word stride
   const int j = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
-  const uint16_t* Vh = V + (size_t)bh * N * D;
+  const TIn* Vh = V + (size_t)bh * N * D;
   uint16_t* VTh = VT + (size_t)bh * D * n_pad;
   for (int c = tid; c < 64 * CH; c += 256) {
     const int key = c / CH, col = (c % CH) * 8, n = j * 64 + key;
-    const u32x4 v = n < N ? ldg16(Vh + (size_t)n * D + col) : (u32x4){0, 0, 0, 0};
+    const u32x4 v = n < N ? load8_bf16(Vh + (size_t)n * D + col) : (u32x4){0, 0, 0, 0};
 #pragma unroll
     for (int p = 0; p < 4; ++p) tile[key][col / 2 + p] = v[p];
   }
@@ -109,29 +106,36 @@ __global__ __launch_bounds__(256) void anchor_pack_vt(const uint16_t* __restrict
   }
 }
 
-template <int D, bool OUT_F32>
-__global__ __launch_bounds__(kThreads, 1) void anchor_bf16(const uint16_t* __restrict__ Q,
-                                                      const uint16_t* __restrict__ K,
-                                                      const uint16_t* __restrict__ V,
-                                                      const uint16_t* __restrict__ G,
+template <int D, bool OUT_F32, typename TIn>
+__global__ __launch_bounds__(kThreads, 1) void anchor_bf16(const TIn* __restrict__ Q,
+                                                      const TIn* __restrict__ K,
+                                                      const TIn* __restrict__ G,
                                                       const uint16_t* __restrict__ VT,
                                                       void* __restrict__ out, int N, int n_pad,
                                                       int nqb, int nmain, int split, float c,
                                                       int accumulate, float* __restrict__ part,
                                                       float* __restrict__ part_ml) {
-  constexpr int NK = D / 16;              // k-steps of S^T
+  constexpr int ES = sizeof(TIn);         // bytes per input element: 2 bf16, 1 fp8
+  constexpr bool F8 = ES == 1;
+  constexpr int CPO = F8 ? 2 : 1;         // 16-byte K chunks per S^T operand
+  constexpr int NK = D * ES / (32 * CPO);  // k-steps of S^T (16 bf16 or 64 fp8 features)
   constexpr int ND = D / 32;              // 32-row blocks of O^T
-  constexpr int CH = D / 8;               // 16-byte chunks per row
-  constexpr int LOADS = kBC * CH / kThreads;  // 16-byte loads per thread per tensor per tile
-  constexpr uint32_t kTileBytes = kBC * D * 2;
-  using Swz = AnchorSwz<D>;
+  constexpr int RB = D * ES;              // bytes per K row
+  constexpr int CH = RB / 16;             // 16-byte chunks per K row
+  constexpr int KBLK = kBC * RB / 1024;   // 1 KB direct-to-LDS blocks per K tile
+  constexpr int LK = KBLK > kWaves ? KBLK / kWaves : 1;  // K blocks per loading wave
+  constexpr int KW = KBLK / LK;           // waves that load K (4 for fp8, D = 64)
+  constexpr int LV = kBC * D * 2 / 1024 / kWaves;        // V^T blocks per wave
+  constexpr int RPB = 1024 / RB;          // K rows per block
+  constexpr uint32_t kTileBytes = kBC * RB;
+  using QOp = std::conditional_t<F8, u32x8, u32x4>;
   // Four separate LDS arrays rather than two [2][...] ones: the compiler then
   // knows that the direct-to-LDS loads filling one buffer do not alias the
   // reads of the other, and does not make every LDS read wait for them.
-  __shared__ __attribute__((aligned(16))) uint16_t Ks0[kBC * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Ks1[kBC * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Ks2[kBC * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Ks3[kBC * D];
+  __shared__ __attribute__((aligned(16))) TIn Ks0[kBC * D];
+  __shared__ __attribute__((aligned(16))) TIn Ks1[kBC * D];
+  __shared__ __attribute__((aligned(16))) TIn Ks2[kBC * D];
+  __shared__ __attribute__((aligned(16))) TIn Ks3[kBC * D];
   __shared__ __attribute__((aligned(16))) uint16_t Vs0[kBC * D];
   __shared__ __attribute__((aligned(16))) uint16_t Vs1[kBC * D];
   __shared__ __attribute__((aligned(16))) uint16_t Vs2[kBC * D];
@@ -139,7 +143,7 @@ __global__ __launch_bounds__(kThreads, 1) void anchor_bf16(const uint16_t* __res
   // buffer b of each tensor: a compile-time b names one array, which lets the
   // compiler keep LDS reads of one buffer independent of the DMA into another;
   // a run-time b (rare edge iterations) selects among them
-  auto kbuf = [&](auto b) -> uint16_t* {
+  auto kbuf = [&](auto b) -> TIn* {
     if constexpr (std::is_integral_v<decltype(b)>) {
       const int x = b & 3;
       return x == 0 ? Ks0 : x == 1 ? Ks1 : x == 2 ? Ks2 : Ks3;
@@ -189,54 +193,68 @@ __global__ __launch_bounds__(kThreads, 1) void anchor_bf16(const uint16_t* __res
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 31, h = lane >> 5;
   const size_t base = (size_t)bh * N * D;
-  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const uint32_t head_bytes = (uint32_t)N * RB;
   const int qrow = qb * kBR + wave * 32 + r;
 
-  u32x4 qf[NK];
+  // Q^T operand of k-step t: query qrow, bytes 32t + 16h (bf16) or 64t + 32h (fp8)
+  QOp qf[NK];
   {
     const rsrc_t Qr = make_rsrc(Q + base, head_bytes);
-    const uint32_t qoff = qrow < N ? (uint32_t)qrow * D * 2 : head_bytes;  // past N reads 0
+    const uint32_t qoff = qrow < N ? (uint32_t)qrow * RB : head_bytes;  // past N reads 0
 #pragma unroll
-    for (int t = 0; t < NK; ++t) qf[t] = buf_load16(Qr, qoff + (16 * t + 8 * h) * 2);
+    for (int t = 0; t < NK; ++t) {
+      if constexpr (F8)
+        qf[t] = concat(buf_load16(Qr, qoff + 64 * t + 32 * h), buf_load16(Qr, qoff + 64 * t + 32 * h + 16));
+      else
+        qf[t] = buf_load16(Qr, qoff + 32 * t + 16 * h);
+    }
   }
 
   // Tiles go global -> LDS directly (buffer_load ... lds): instruction i of
-  // wave w fills the 1 KB LDS block bw = LOADS*w + i in lane order. K tiles hold
-  // 4 key rows of 256 B per block (8 of 128 B for D=64): lane l lands in row
-  // 4bw + l/16, physical chunk l%16. V^T tiles hold 8 feature rows of 128 B (64
-  // keys) per block: lane l lands in row 8bw + l/8, physical chunk l%8. Each lane
-  // fetches the logical chunk that the swizzle puts there.
-  constexpr int ROWS_PER_BLK = 1024 / (D * 2);
-  uint32_t goff_k[LOADS], goff_v[LOADS];
+  // wave w fills 1 KB LDS block bw = L*w + i in lane order. K tiles hold RPB key
+  // rows of RB bytes per block (4 x 256 B for bf16 D=128, 8 x 128 B for bf16
+  // D=64 and fp8 D=128, 16 x 64 B for fp8 D=64): lane l lands in row
+  // RPB bw + l/CH, physical chunk l%CH. V^T tiles hold 8 feature rows of 128 B
+  // (64 bf16 keys) per block: lane l lands in row 8bw + l/8, physical chunk l%8.
+  // Each lane fetches the logical chunk that the swizzle puts there.
+  uint32_t goff_k[LK], goff_v[LV];
 #pragma unroll
-  for (int i = 0; i < LOADS; ++i) {
-    const int blk = LOADS * wave + i;
-    const int row = blk * ROWS_PER_BLK + lane / CH, pc = lane % CH;
-    goff_k[i] = (row * D + ((pc ^ (row & Swz::kmask)) * 8)) * 2;
-    const int vd = blk * 8 + (lane >> 3), vpc = lane & 7;
+  for (int i = 0; i < LK; ++i) {
+    const int row = (LK * wave + i) * RPB + lane / CH, pc = lane % CH;
+    goff_k[i] = row * RB + (pc ^ k_swz<CH>(row)) * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < LV; ++i) {
+    const int vd = (LV * wave + i) * 8 + (lane >> 3), vpc = lane & 7;
     goff_v[i] = ((uint32_t)vd * n_pad + ((vpc ^ vt_swz(vd)) * 8)) * 2;
   }
   const uint32_t vt_head_bytes = (uint32_t)D * n_pad * 2;
   // issue K (or V^T) tile j into LDS buffer buf (completion: wait_all_memory + barrier)
   auto load_k = [&](int j, auto buf_c) {
+    if (KW < kWaves && wave >= KW) return;  // wave-uniform
     const uint32_t done = (uint32_t)j * kTileBytes;
     const uint32_t left = done < head_bytes ? head_bytes - done : 0u;
     const rsrc_t kr = make_rsrc_uniform(K + base + (size_t)j * kBC * D, left);
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) buf_load16_lds(kr, goff_k[i], kbuf(buf_c) + (LOADS * wave + i) * 512);
+    for (int i = 0; i < LK; ++i)
+      buf_load16_lds(kr, goff_k[i], kbuf(buf_c) + (LK * wave + i) * (1024 / ES));
   };
   auto load_v = [&](int j, auto buf_c) {
     const uint32_t done = (uint32_t)j * kBC * 2;
     const uint32_t left = j * kBC < n_pad ? vt_head_bytes - done : 0u;
     const rsrc_t vr = make_rsrc_uniform(VT + (size_t)bh * D * n_pad + (size_t)j * kBC, left);
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) buf_load16_lds(vr, goff_v[i], vbuf(buf_c) + (LOADS * wave + i) * 512);
+    for (int i = 0; i < LV; ++i) buf_load16_lds(vr, goff_v[i], vbuf(buf_c) + (LV * wave + i) * 512);
   };
 
-  // S^T operand A (key rows): lane reads row kb*32 + r, chunk 2t + h (swizzled)
-  int koff[NK];
+  // S^T operand A (key rows): lane reads row kb*32 + r, logical chunks
+  // CPO (2t + h) + u, u < CPO (swizzled); offsets in elements
+  int koff[NK][CPO];
 #pragma unroll
-  for (int t = 0; t < NK; ++t) koff[t] = r * D + (((2 * t + h) ^ (r & Swz::kmask)) * 8);
+  for (int t = 0; t < NK; ++t)
+#pragma unroll
+    for (int u = 0; u < CPO; ++u)
+      koff[t][u] = r * D + ((CPO * (2 * t + h) + u) ^ k_swz<CH>(r)) * (16 / ES);
   // O^T operand A (V^T rows): MFMA row r of block b is feature
   // d = 32b + vrow, vrow = 16((r>>2)&1) + 4(r>>3) + (r&3), so each lane ends with
   // 16 consecutive output features; its 8 keys of k-step ks are logical chunk
@@ -259,15 +277,20 @@ __global__ __launch_bounds__(kThreads, 1) void anchor_bf16(const uint16_t* __res
   // ---- building blocks -----------------------------------------------------
   // S^T of the tile held in K buffer KB (two 32-key blocks)
   auto s_tile = [&](auto kb_c, f32x16* s) {
-    const uint16_t* Kb = kbuf(kb_c);
+    const TIn* Kb = kbuf(kb_c);
     s[0] = (f32x16){};
     s[1] = (f32x16){};
 #pragma unroll
     for (int t = 0; t < NK; ++t) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(&Kb[kb * 32 * D + koff[t]]);
-        s[kb] = mfma32x32x16(a, qf[t], s[kb]);
+        const u32x4 a = *reinterpret_cast<const u32x4*>(&Kb[kb * 32 * D + koff[t][0]]);
+        if constexpr (F8) {
+          const u32x4 a1 = *reinterpret_cast<const u32x4*>(&Kb[kb * 32 * D + koff[t][1]]);
+          s[kb] = mfma32x32x64_fp8(concat(a, a1), qf[t], s[kb]);
+        } else {
+          s[kb] = mfma32x32x16(a, qf[t], s[kb]);
+        }
       }
     }
   };
@@ -463,15 +486,10 @@ __global__ __launch_bounds__(kThreads, 1) void anchor_bf16(const uint16_t* __res
 #pragma unroll
   for (int b = 0; b < ND; ++b) {
     const size_t off = base + (size_t)qrow * D + 32 * b + 16 * h;
-    const u32x4 g0 = ldg16(G + off), g1 = ldg16(G + off + 8);
     float o[16];
+    load16_f32(G + off, o);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      o[2 * p] = (acc[b][2 * p] * inv) * sigmoid(bf_lo(g0[p]));
-      o[2 * p + 1] = (acc[b][2 * p + 1] * inv) * sigmoid(bf_hi(g0[p]));
-      o[8 + 2 * p] = (acc[b][8 + 2 * p] * inv) * sigmoid(bf_lo(g1[p]));
-      o[8 + 2 * p + 1] = (acc[b][8 + 2 * p + 1] * inv) * sigmoid(bf_hi(g1[p]));
-    }
+    for (int x = 0; x < 16; ++x) o[x] = (acc[b][x] * inv) * sigmoid(o[x]);
     if (OUT_F32) {
       float* dst = reinterpret_cast<float*>(out) + off;
 #pragma unroll
@@ -507,10 +525,10 @@ __global__ __launch_bounds__(kThreads, 1) void anchor_bf16(const uint16_t* __res
 // gate and the store, as in the main epilogue. Each thread takes 8 features of
 // one query row; 16 rows per workgroup, kBR / 16 workgroups per split block.
 // ---------------------------------------------------------------------------
-template <int D, bool OUT_F32>
+template <int D, bool OUT_F32, typename TIn>
 __global__ __launch_bounds__(256) void anchor_combine(const float* __restrict__ part,
                                                       const float* __restrict__ part_ml,
-                                                      const uint16_t* __restrict__ G,
+                                                      const TIn* __restrict__ G,
                                                       void* __restrict__ out, int N, int nqb,
                                                       int nmain, int split, int accumulate) {
   constexpr int TPR = D / 8;                 // threads per row
@@ -542,12 +560,10 @@ __global__ __launch_bounds__(256) void anchor_combine(const float* __restrict__ 
   }
   const float inv = 1.0f / wsum;
   const size_t base = ((size_t)bh * N + qrow) * D + f;
-  const u32x4 gv = ldg16(G + base);
+  float gf[8];
+  load8_f32(G + base, gf);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    o[2 * e] = (o[2 * e] * inv) * sigmoid(bf_lo(gv[e]));
-    o[2 * e + 1] = (o[2 * e + 1] * inv) * sigmoid(bf_hi(gv[e]));
-  }
+  for (int e = 0; e < 8; ++e) o[e] = (o[e] * inv) * sigmoid(gf[e]);
   if (OUT_F32) {
     float* dst = reinterpret_cast<float*>(out) + base;
     f32x4 lo = (f32x4){o[0], o[1], o[2], o[3]}, hi = (f32x4){o[4], o[5], o[6], o[7]};
@@ -604,7 +620,7 @@ AnchorLayout anchor_layout(const hla_dims& d) {
   return L;
 }
 
-template <int D>
+template <int D, typename TIn>
 hipError_t launch_d(const hla_dims& d, const void* q, const void* k, const void* v, const void* g,
                     void* out, int accumulate, float scale, void* ws, hipStream_t stream) {
   const int BH = int(d.B * d.H), N = int(d.N);
@@ -634,24 +650,23 @@ hipError_t launch_d(const hla_dims& d, const void* q, const void* k, const void*
   }
   const int nmain = total - tail;
   const int grid = nmain + tail * split;
-  hipLaunchKernelGGL(anchor_pack_vt<D>, dim3(n_pad / kBC, BH), dim3(256), 0, stream,
-                     reinterpret_cast<const uint16_t*>(v), vt, N, n_pad);
-  const uint16_t* Qp = reinterpret_cast<const uint16_t*>(q);
-  const uint16_t* Kp = reinterpret_cast<const uint16_t*>(k);
-  const uint16_t* Vp = reinterpret_cast<const uint16_t*>(v);
-  const uint16_t* Gp = reinterpret_cast<const uint16_t*>(g);
+  hipLaunchKernelGGL((anchor_pack_vt<D, TIn>), dim3(n_pad / kBC, BH), dim3(256), 0, stream,
+                     reinterpret_cast<const TIn*>(v), vt, N, n_pad);
+  const TIn* Qp = reinterpret_cast<const TIn*>(q);
+  const TIn* Kp = reinterpret_cast<const TIn*>(k);
+  const TIn* Gp = reinterpret_cast<const TIn*>(g);
   if (d.out_dtype == HLA_F32) {
-    hipLaunchKernelGGL((anchor_bf16<D, true>), dim3(grid), dim3(kThreads), 0, stream, Qp, Kp, Vp,
+    hipLaunchKernelGGL((anchor_bf16<D, true, TIn>), dim3(grid), dim3(kThreads), 0, stream, Qp, Kp,
                        Gp, vt, out, N, n_pad, nqb, nmain, split, c, accumulate, part, part_ml);
     if (tail > 0)
-      hipLaunchKernelGGL((anchor_combine<D, true>), dim3(tail * (D / 8)), dim3(256), 0, stream,
+      hipLaunchKernelGGL((anchor_combine<D, true, TIn>), dim3(tail * (D / 8)), dim3(256), 0, stream,
                          part, part_ml, Gp, out, N, nqb, nmain, split, accumulate);
   } else {
-    hipLaunchKernelGGL((anchor_bf16<D, false>), dim3(grid), dim3(kThreads), 0, stream, Qp, Kp, Vp,
+    hipLaunchKernelGGL((anchor_bf16<D, false, TIn>), dim3(grid), dim3(kThreads), 0, stream, Qp, Kp,
                        Gp, vt, out, N, n_pad, nqb, nmain, split, c, accumulate, part, part_ml);
     if (tail > 0)
-      hipLaunchKernelGGL((anchor_combine<D, false>), dim3(tail * (D / 8)), dim3(256), 0, stream,
-                         part, part_ml, Gp, out, N, nqb, nmain, split, accumulate);
+      hipLaunchKernelGGL((anchor_combine<D, false, TIn>), dim3(tail * (D / 8)), dim3(256), 0,
+                         stream, part, part_ml, Gp, out, N, nqb, nmain, split, accumulate);
   }
   return hipGetLastError();
 }
@@ -659,15 +674,19 @@ hipError_t launch_d(const hla_dims& d, const void* q, const void* k, const void*
 }  // namespace
 
 size_t anchor_workspace_bytes(const hla_dims& d) {
-  if (d.in_dtype != HLA_BF16) return 0;
+  if (d.in_dtype == HLA_F32) return 0;
   return anchor_layout(d).total;
 }
 
 hipError_t launch_anchor_bf16(const hla_dims& d, const void* q, const void* k, const void* v,
                               const void* g, void* out, int accumulate, float scale, void* ws,
                               hipStream_t stream) {
-  if (d.D == 128) return launch_d<128>(d, q, k, v, g, out, accumulate, scale, ws, stream);
-  return launch_d<64>(d, q, k, v, g, out, accumulate, scale, ws, stream);
+  if (d.in_dtype == HLA_FP8_E4M3) {
+    if (d.D == 128) return launch_d<128, uint8_t>(d, q, k, v, g, out, accumulate, scale, ws, stream);
+    return launch_d<64, uint8_t>(d, q, k, v, g, out, accumulate, scale, ws, stream);
+  }
+  if (d.D == 128) return launch_d<128, uint16_t>(d, q, k, v, g, out, accumulate, scale, ws, stream);
+  return launch_d<64, uint16_t>(d, q, k, v, g, out, accumulate, scale, ws, stream);
 }
 
 }  // namespace hla

@@ -182,7 +182,6 @@ hla_status hla_softmax_anchor_fwd(const hla_dims* d, const void* q, const void* 
   if (st != HLA_OK) return st;
   if (!isfinite(scale) || scale <= 0.f || (accumulate != 0 && accumulate != 1))
     return HLA_ERR_BAD_ARG;
-  if (d->in_dtype == HLA_FP8_E4M3) return HLA_ERR_UNSUPPORTED;
   if (empty(d)) return HLA_OK;
   if ((st = check_tensors(q, k, v, g, out)) != HLA_OK) return st;
   const size_t need = anchor_workspace_bytes(*d);
@@ -193,7 +192,7 @@ hla_status hla_softmax_anchor_fwd(const hla_dims* d, const void* q, const void* 
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   clear_pending_error();
-  if (d->in_dtype == HLA_BF16)
+  if (d->in_dtype != HLA_F32)
     return from_hip(launch_anchor_bf16(*d, q, k, v, g, out, accumulate, scale, workspace, s));
   return from_hip(launch_anchor_f32(*d, q, k, v, g, out, accumulate, scale, s));
 }
@@ -214,7 +213,6 @@ hla_status hla_hybrid_stack_fwd(const hla_dims* d, int n_layers, const int32_t* 
     any_linear |= kinds[l] == HLA_LAYER_LINEAR;
     any_softmax |= kinds[l] == HLA_LAYER_SOFTMAX;
   }
-  if (any_softmax && d->in_dtype == HLA_FP8_E4M3) return HLA_ERR_UNSUPPORTED;
   if (empty(d)) return HLA_OK;
   for (int l = 0; l < n_layers; ++l)
     if ((st = check_tensors(q[l], k[l], v[l], g[l], x)) != HLA_OK) return st;
@@ -231,7 +229,7 @@ hla_status hla_hybrid_stack_fwd(const hla_dims* d, int n_layers, const int32_t* 
     if (workspace_bytes < need) return HLA_ERR_WORKSPACE;
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const bool bf = d->in_dtype != HLA_F32;  // bf16, or fp8 (linear layers only)
+  const bool bf = d->in_dtype != HLA_F32;  // bf16 or fp8 kernels
   clear_pending_error();
   for (int l = 0; l < n_layers; ++l) {
     hipError_t e;

@@ -53,6 +53,21 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+// D = A(32x64) * B(64x32) + C with OCP fp8 e4m3 operands: lane l holds row
+// (A) or column (B) l % 32, k = 32 (l / 32) + byte index of the 8 dwords. The
+// products are exact in fp32; the zero format/scale arguments select the
+// plain (unscaled) fp8 instruction.
+__device__ __forceinline__ f32x16 mfma32x32x64_fp8(u32x8 a, u32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(__builtin_bit_cast(i32x8, a),
+                                                         __builtin_bit_cast(i32x8, b), c, 0, 0, 0,
+                                                         0, 0, 0);
+}
+__device__ __forceinline__ u32x8 concat(u32x4 lo, u32x4 hi) {
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // 2^x on the transcendental unit (v_exp_f32).
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -133,7 +148,6 @@ __device__ __forceinline__ void stg16(void* p, u32x4 v) { *reinterpret_cast<u32x
 // Every e4m3 value is exactly representable in bf16 (4-bit exponent, 3-bit
 // mantissa), so fp8 inputs convert losslessly into the bf16 operands the
 // kernels already use.
-typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 
 // four fp8 bytes -> four floats (bytes 0,1 then 2,3), exact
 __device__ __forceinline__ f32x4 fp8x4_to_f32(uint32_t w) {
@@ -163,6 +177,41 @@ __device__ __forceinline__ u32x4 load8_bf16_stream(const T* p) {
   if constexpr (sizeof(T) == 1)
     return fp8x8_to_bf16(__builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p)));
   else return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+// Eight / sixteen consecutive elements of a bf16 or fp8 tensor as floats.
+template <typename T>
+__device__ __forceinline__ void load8_f32(const T* p, float* o) {
+  if constexpr (sizeof(T) == 1) {
+    const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const f32x4 f = fp8x4_to_f32(w[q]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[4 * q + e] = f[e];
+    }
+  } else {
+    const u32x4 w = ldg16(p);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      o[2 * q] = bf_lo(w[q]);
+      o[2 * q + 1] = bf_hi(w[q]);
+    }
+  }
+}
+template <typename T>
+__device__ __forceinline__ void load16_f32(const T* p, float* o) {
+  if constexpr (sizeof(T) == 1) {
+    const u32x4 w = ldg16(p);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 f = fp8x4_to_f32(w[q]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[4 * q + e] = f[e];
+    }
+  } else {
+    load8_f32(p, o);
+    load8_f32(p + 8, o + 8);
+  }
 }
 // One element of a bf16 or fp8 tensor as float.
 template <typename T>

@@ -143,8 +143,8 @@ def test_write_gated_argument_errors():
 
 
 def test_fp8_inputs():
-    # fp8 inputs are built for the linear calls; they take the bf16 path's
-    # workspace (the state is formed from the same values)
+    # fp8 inputs take the bf16 paths' workspaces (the same values, converted
+    # on load)
     for o in (BF16, F32):
         for D in (64, 128):
             assert hla.hla_linear_workspace_bytes(dims(D=D, i=FP8, o=o)) == \
@@ -154,6 +154,12 @@ def test_fp8_inputs():
     assert lin_w(d, w=None) == NULLP
     assert lin(d, wsb=hla.hla_linear_workspace_bytes(d) - 1) == WS
     assert stack(dims(i=FP8, o=F32), kinds=(0, 0), ws=None) == NULLP
+    # the anchor repacks V into bf16 V^T for fp8 inputs too: same workspace
+    for (N, D) in [(19320, 128), (1000, 64)]:
+        assert hla.hla_softmax_anchor_workspace_bytes(dims(N=N, D=D, i=FP8)) == \
+            hla.hla_softmax_anchor_workspace_bytes(dims(N=N, D=D, i=BF16))
+    assert sm(d, ws=None) == NULLP
+    assert sm(d, wsb=hla.hla_softmax_anchor_workspace_bytes(d) - 1) == WS
 
 
 def test_softmax_argument_errors():

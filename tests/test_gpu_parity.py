@@ -488,3 +488,65 @@ def test_linear_fp8_full_720p():
     e = rel_err(got, oracle.gated_linear(q, k, v, g, w.eps))
     print(f"[720p_81f fp8] linear err {e:.3e}", flush=True)
     assert e <= 2e-2
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("D", [128, 64])
+@pytest.mark.parametrize("N", [1, 63, 65, 257, 1000])
+def test_softmax_fp8_tails(N, D, out_dtype):
+    # Q K^T on the fp8 matrix cores, P V in bf16
+    q, k, v, g = make((1, 2, N, D), 11000 + N + D, FP8)
+    got = run_softmax(q, k, v, g, out_dtype=out_dtype)
+    assert got.dtype == out_dtype
+    assert rel_err(got, oracle.gated_softmax(q, k, v, g, D ** -0.5)) <= TOL[torch.bfloat16]
+
+
+def test_softmax_fp8_close_to_bf16_path_on_same_values():
+    # both paths see the same values; only the fp32 summation order of Q K^T
+    # differs, so the outputs agree far inside the bf16 bar
+    q, k, v, g = make((2, 2, 1500, 128), 11100, FP8)
+    a = run_softmax(q, k, v, g, out_dtype=torch.float32)
+    b = run_softmax(*[t.to(torch.bfloat16) for t in (q, k, v, g)], out_dtype=torch.float32)
+    assert rel_err(a, oracle.as_f64(b.cpu())) <= 2e-3
+
+
+def test_softmax_fp8_split_and_accumulate():
+    # the key-split last batch with the combine kernel, plain and into fp32
+    B, H, N, D = 1, 3, 2000, 128
+    q, k, v, g = make((B, H, N, D), 11200, FP8)
+    ref = oracle.gated_softmax(q, k, v, g, D ** -0.5)
+    assert rel_err(run_softmax(q, k, v, g), ref) <= TOL[torch.bfloat16]
+    base = custom((B, H, N, D), 11300, torch.float32, n=1)[0]
+    acc = base.to(DEV)
+    run_softmax(q, k, v, g, accumulate=True, out=acc)
+    assert rel_err(acc.cpu() - base, ref) <= TOL[torch.bfloat16]
+
+
+def test_softmax_fp8_peaky_logits():
+    # large scores: one key dominates most rows, probabilities span many octaves
+    q, k, v, g = make((1, 2, 700, 128), 11400, torch.float32)
+    q8, k8, v8, g8 = ((q * 4).to(FP8), k.to(FP8), v.to(FP8), g.to(FP8))
+    got = run_softmax(q8, k8, v8, g8)
+    assert rel_err(got, oracle.gated_softmax(q8, k8, v8, g8, 128 ** -0.5)) <= TOL[torch.bfloat16]
+
+
+def test_hybrid_stack_fp8_small_full():
+    B, H, N, D = 1, 2, 777, 128
+    kinds = oracle.hybrid_kinds(4)
+    layers = [make((B, H, N, D), 11500 + 10 * l, FP8) for l in range(4)]
+    x0 = custom((B, H, N, D), 11600, torch.float32, n=1)[0]
+    x = x0.to(DEV)
+    hla.hla_hybrid_stack_fwd(x, [tuple(t.to(DEV) for t in L) for L in layers], kinds)
+    torch.cuda.synchronize()
+    ref = oracle.hybrid_stack(x0, layers, kinds, 1e-6, D ** -0.5)
+    assert rel_err(x.cpu() - x0, ref - oracle.as_f64(x0)) <= 2e-2
+
+
+def test_softmax_fp8_full_720p_sampled():
+    w = BY_NAME["720p_81f"]
+    q, k, v, g = layer_inputs(w, 0, dtype=FP8)
+    rows = sample_rows(w.N, seed=81)
+    sm = run_softmax(q, k, v, g, w.scale)
+    e = rel_err(sm[..., rows, :], oracle.gated_softmax(q, k, v, g, w.scale, rows=rows))
+    print(f"[720p_81f fp8] softmax err {e:.3e} on {len(rows)} rows", flush=True)
+    assert e <= TOL[torch.bfloat16]

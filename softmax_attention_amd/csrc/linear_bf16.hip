@@ -1,4 +1,4 @@
-// Gated linear attention, bf16 inputs, on gfx950 matrix cores.
+// Gated linear attention, bf16 or fp8 (OCP e4m3) inputs, on gfx950 matrix cores.
 //
 // Three launches per call:
 //   1. state pass   per (token chunk, b, h): S_c = phi(K_c)^T V_c and
@@ -20,7 +20,47 @@
 namespace hla {
 namespace {
 
-constexpr int kTile = 64;  // tokens per LDS tile in the state pass
+// fp8 inputs are converted exactly to bf16 where a kernel consumes them, not
+// where it loads them, so the loads of the next tile stay in flight meanwhile.
+// Every global load is 16 bytes: 8 bf16 or 16 fp8 elements.
+__device__ __forceinline__ u32x4 fp8_half(u32x4 raw, int hi) {
+  return fp8x8_to_bf16(hi ? (u32x2){raw[2], raw[3]} : (u32x2){raw[0], raw[1]});
+}
+
+// ---------------------------------------------------------------------------
+// Operand fragments of the output pass (16x16x32 MFMA: A rows i = lane & 15,
+// k = 8*(lane>>4) + e). Numerator fragment (jb, t) holds A[i][k] =
+// S[row(t, k)][col(jb, i)], ordered so that an output lane's Q slice (its B
+// operand) and its output features are whole 16-byte runs of its token's row:
+//   bf16 (8 features per run):  row = 32t + k,
+//                               col = 32(jb>>1) + 8(i>>2) + 4(jb&1) + (i&3);
+//   fp8 (16 features per run):  row = 64(t>>1) + 16(k>>3) + 8(t&1) + (k&7),
+//                               col = 64(jb>>2) + 16(i>>2) + 4(jb&3) + (i&3).
+// frag_pos gives the fp32 slot of S[row][col] among the D*D partial-state
+// slots: ((jb * D/32 + t) * 64 + lane) * 8 + e, lane = 16(k>>3) + i, e = k&7.
+// ---------------------------------------------------------------------------
+template <int D, bool F8>
+__device__ __forceinline__ int frag_pos(int row, int col) {
+  constexpr int NT = D / 32;
+  int t, kg, jb, i;
+  if constexpr (F8) {
+    t = 2 * (row >> 6) + ((row >> 3) & 1);
+    kg = (row >> 4) & 3;
+    jb = 4 * (col >> 6) + ((col >> 2) & 3);
+    i = 4 * ((col >> 4) & 3) + (col & 3);
+  } else {
+    t = row >> 5;
+    kg = (row >> 3) & 3;
+    jb = 2 * (col >> 5) + ((col >> 2) & 1);
+    i = 4 * ((col >> 3) & 3) + (col & 3);
+  }
+  return ((jb * NT + t) * 64 + 16 * kg + i) * 8 + (row & 7);
+}
+// first z entry of the 8 that k-step t, k-group kg of a denominator fragment holds
+template <int D, bool F8>
+__device__ __forceinline__ int z_run(int t, int kg) {
+  return F8 ? 64 * (t >> 1) + 16 * kg + 8 * (t & 1) : 32 * t + 8 * kg;
+}
 
 // ---------------------------------------------------------------------------
 // 1. state pass
@@ -28,24 +68,28 @@ constexpr int kTile = 64;  // tokens per LDS tile in the state pass
 // Wave w owns a (D/2 x D/2) quadrant of S: 32-row blocks [(w>>1)*RB, +RB) and
 // 32-column blocks [(w&1)*RB, +RB). MFMA operand A is phi(K)^T (rows = features,
 // k = tokens) and B is V (k = tokens, cols = features); both read 8 tokens of one
-// feature per lane out of a row-major LDS tile.
+// feature per lane out of a row-major bf16 LDS tile.
 // With WG (the write-gated variant) each token's phi(K) row is first scaled by
-// its write strength sigma(W_n), W one bf16 logit per token and head ([B,H,N]);
-// the scaled row, rounded to bf16, feeds both the MFMA and the normaliser sum.
-// TIn: uint16_t for bf16 inputs, uint8_t for fp8 (e4m3) inputs, converted
-// exactly to bf16 as they are loaded.
+// its write strength sigma(W_n), W one logit per token and head ([B,H,N]); the
+// scaled row, rounded to bf16, feeds both the MFMA and the normaliser sum.
+// TIn: uint16_t for bf16 inputs, uint8_t for fp8; an fp8 tile holds 128 tokens
+// so that a tile is the same number of bytes (and 16-byte loads) either way.
 template <int D, bool WG, typename TIn>
 __global__ __launch_bounds__(256) void linear_state_bf16(const TIn* __restrict__ K,
                                                          const TIn* __restrict__ V,
                                                          const TIn* __restrict__ W,
                                                          float* __restrict__ part, int N, int T,
                                                          int C) {
-  constexpr int CH = D / 8;                // 16-byte chunks per token row
-  constexpr int LOADS = kTile * CH / 256;  // 16-byte loads per thread per tensor per tile
+  constexpr bool F8 = sizeof(TIn) == 1;
+  constexpr int EPL = 16 / sizeof(TIn);    // elements per 16-byte load
+  constexpr int HALVES = EPL / 8;          // bf16 operands per load
+  constexpr int CH = D / EPL;              // loads per token row
+  constexpr int TILE = 64 * HALVES;        // tokens per LDS tile
+  constexpr int LOADS = TILE * CH / 256;   // loads per thread per tensor per tile
   constexpr int RS = D + 8;                // LDS row stride in elements (pads banks)
   constexpr int RB = D / 64;               // 32-wide blocks per wave per side
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kTile * RS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[kTile * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[TILE * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[TILE * RS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = blockIdx.x, bh = blockIdx.y;
@@ -55,12 +99,12 @@ __global__ __launch_bounds__(256) void linear_state_bf16(const TIn* __restrict__
   const TIn* Kh = K + base;
   const TIn* Vh = V + base;
 
-  u32x4 kr[LOADS], vr[LOADS];
+  u32x4 kr[LOADS], vr[LOADS];  // raw bytes as loaded
   TIn wr[LOADS];
   const TIn* Wh = WG ? W + (size_t)bh * N : nullptr;
-  float zacc[8];
+  float zacc[EPL];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) zacc[e] = 0.f;
+  for (int e = 0; e < EPL; ++e) zacc[e] = 0.f;
   f32x16 acc[RB][RB];
 #pragma unroll
   for (int x = 0; x < RB; ++x)
@@ -71,10 +115,10 @@ __global__ __launch_bounds__(256) void linear_state_bf16(const TIn* __restrict__
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int chunk = tid + 256 * i;
-      const int n = t0 + chunk / CH, col = (chunk % CH) * 8;
+      const int n = t0 + chunk / CH, col = (chunk % CH) * EPL;
       if (n < n1) {
-        kr[i] = load8_bf16_stream(Kh + (size_t)n * D + col);
-        vr[i] = load8_bf16_stream(Vh + (size_t)n * D + col);
+        kr[i] = ldg16_stream(Kh + (size_t)n * D + col);
+        vr[i] = ldg16_stream(Vh + (size_t)n * D + col);
         if (WG) wr[i] = Wh[n];
       } else {
         kr[i] = (u32x4){0, 0, 0, 0};
@@ -86,7 +130,7 @@ __global__ __launch_bounds__(256) void linear_state_bf16(const TIn* __restrict__
 
   const int r = lane & 31, h = lane >> 5;
   const int ib0 = (wave >> 1) * RB, jb0 = (wave & 1) * RB;
-  const int ntiles = (n1 - n0 + kTile - 1) / kTile;
+  const int ntiles = (n1 - n0 + TILE - 1) / TILE;
 
   load_tile(n0);
   for (int it = 0; it < ntiles; ++it) {
@@ -94,25 +138,30 @@ __global__ __launch_bounds__(256) void linear_state_bf16(const TIn* __restrict__
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int chunk = tid + 256 * i;
-      const int row = chunk / CH, col = (chunk % CH) * 8;
-      u32x4 kk = relu_bf16x8(kr[i]);
-      if (WG) {
-        const float beta = sigmoid(elem_f32(wr[i]));
+      const int row = chunk / CH, col = (chunk % CH) * EPL;
+      float beta = 1.f;
+      if (WG) beta = sigmoid(elem_f32(wr[i]));
 #pragma unroll
-        for (int p = 0; p < 4; ++p) kk[p] = pack_bf16(bf_lo(kk[p]) * beta, bf_hi(kk[p]) * beta);
-      }
+      for (int hh = 0; hh < HALVES; ++hh) {
+        u32x4 kk = relu_bf16x8(F8 ? fp8_half(kr[i], hh) : kr[i]);
+        const u32x4 vv = F8 ? fp8_half(vr[i], hh) : vr[i];
+        if (WG) {
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        zacc[2 * p] += bf_lo(kk[p]);
-        zacc[2 * p + 1] += bf_hi(kk[p]);
+          for (int p = 0; p < 4; ++p) kk[p] = pack_bf16(bf_lo(kk[p]) * beta, bf_hi(kk[p]) * beta);
+        }
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          zacc[8 * hh + 2 * p] += bf_lo(kk[p]);
+          zacc[8 * hh + 2 * p + 1] += bf_hi(kk[p]);
+        }
+        *reinterpret_cast<u32x4*>(&Ks[row * RS + col + 8 * hh]) = kk;
+        *reinterpret_cast<u32x4*>(&Vs[row * RS + col + 8 * hh]) = vv;
       }
-      *reinterpret_cast<u32x4*>(&Ks[row * RS + col]) = kk;
-      *reinterpret_cast<u32x4*>(&Vs[row * RS + col]) = vr[i];
     }
     __syncthreads();
-    if (it + 1 < ntiles) load_tile(n0 + (it + 1) * kTile);  // in flight during the MFMAs
+    if (it + 1 < ntiles) load_tile(n0 + (it + 1) * TILE);  // in flight during the MFMAs
 #pragma unroll
-    for (int s = 0; s < kTile / 16; ++s) {
+    for (int s = 0; s < TILE / 16; ++s) {
       const int tok = 16 * s + 8 * h;
       u32x4 a[RB], b[RB];
 #pragma unroll
@@ -134,54 +183,44 @@ __global__ __launch_bounds__(256) void linear_state_bf16(const TIn* __restrict__
     }
   }
 
-  // partial S, stored in the output pass's fragment order (fp32): element
-  // (row, col) goes to fragment (jb', t) = (2(col>>5) + ((col>>2)&1), row>>5),
-  // lane (g', i') = ((row>>3)&3, 4((col>>3)&3) + (col&3)), slot e' = row&7, so
-  // the reduce reads and writes whole fragments contiguously. C-tile element
+  // partial S, stored in the output pass's fragment order (fp32, see frag_pos)
+  // so the reduce reads and writes whole fragments contiguously. C-tile element
   // (q*4 + e) of lane (col r, half h) is row q*8 + 4h + e: 4 consecutive slots.
   float* P = part + ((size_t)bh * C + c) * (size_t)(D * D + D);
-  constexpr int NT = D / 32;
 #pragma unroll
   for (int x = 0; x < RB; ++x)
 #pragma unroll
-    for (int y = 0; y < RB; ++y) {
-      const int t = ib0 + x;
-      const int jbp = 2 * (jb0 + y) + ((r >> 2) & 1);
-      const int ip = 4 * ((r >> 3) & 3) + (r & 3);
+    for (int y = 0; y < RB; ++y)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int idx = ((jbp * NT + t) * 64 + q * 16 + ip) * 8 + 4 * h;
-        *reinterpret_cast<f32x4*>(&P[idx]) =
+        const int row = (ib0 + x) * 32 + 8 * q + 4 * h, col = (jb0 + y) * 32 + r;
+        *reinterpret_cast<f32x4*>(&P[frag_pos<D, F8>(row, col)]) =
             (f32x4){acc[x][y][q * 4], acc[x][y][q * 4 + 1], acc[x][y][q * 4 + 2], acc[x][y][q * 4 + 3]};
       }
-    }
 
   // partial z: thread tid always loaded feature chunk (tid % CH); sum the
   // 256/CH threads of each chunk in a fixed order
   __syncthreads();
-  float* zred = reinterpret_cast<float*>(Ks);  // 8 KB, fits in the K tile
+  float* zred = reinterpret_cast<float*>(Ks);  // 256 * EPL floats fit in the K tile
 #pragma unroll
-  for (int e = 0; e < 8; ++e) zred[tid * 8 + e] = zacc[e];
+  for (int e = 0; e < EPL; ++e) zred[tid * EPL + e] = zacc[e];
   __syncthreads();
   if (tid < D) {
-    const int cc = tid / 8, e = tid % 8;
-    float s = 0.f;
-    for (int m = 0; m < 256 / CH; ++m) s += zred[(cc + CH * m) * 8 + e];
-    P[D * D + tid] = s;
+    const int cc = tid / EPL, e = tid % EPL;
+    float sum = 0.f;
+    for (int m = 0; m < 256 / CH; ++m) sum += zred[(cc + CH * m) * EPL + e];
+    P[D * D + tid] = sum;
   }
 }
 
 // ---------------------------------------------------------------------------
 // 2. fixed-order reduce of the partial states into output-pass fragments
 // ---------------------------------------------------------------------------
-// Output pass MFMA (16x16x32): A rows i = lane & 15, k = 8*(lane>>4) + e.
-// Fragment (jb, t) of the numerator holds A[i][k] = S[32t + k][f(jb, i)] with
-// f(jb, i) = 32*(jb>>1) + 8*(i>>2) + 4*(jb&1) + (i&3), so that each output lane
-// ends with 8 consecutive features; the state pass already stored its partials
-// in this order. Fragment (NJ, t) of the denominator holds z_hi[32t + k] in
-// rows 0..7 and z_lo[32t + k] in rows 8..15. Chunks are summed in order
+// The state pass already stored its partials in the numerator fragments' order
+// (frag_pos). Fragment (NJ, t) of the denominator holds z_hi[row(t, k)] in rows
+// 0..7 and z_lo[row(t, k)] in rows 8..15. Chunks are summed in order
 // c = 0, 1, ..., C-1 (four independent loads in flight per step).
-template <int D>
+template <int D, bool F8>
 __global__ __launch_bounds__(256) void linear_reduce_bf16(const float* __restrict__ part,
                                                           uint32_t* __restrict__ state, int C) {
   constexpr int NT = D / 32, NJ = D / 16, NF = (NJ + 1) * NT;
@@ -224,7 +263,7 @@ __global__ __launch_bounds__(256) void linear_reduce_bf16(const float* __restric
         (u32x4){pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]), pack_bf16(v[4], v[5]), pack_bf16(v[6], v[7])};
   } else if (tid < NT * 64) {
     const int t = tid >> 6, l = tid & 63, i = l & 15, g = l >> 4;
-    sum8((size_t)D * D + 32 * t + 8 * g, v);
+    sum8((size_t)D * D + z_run<D, F8>(t, g), v);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float hi = bf16_to_f32(f32_to_bf16(v[e]));
@@ -239,17 +278,21 @@ __global__ __launch_bounds__(256) void linear_reduce_bf16(const float* __restric
 // 3. output pass
 // ---------------------------------------------------------------------------
 // Each wave takes 16 tokens at a time. Lane (n = lane & 15, g = lane >> 4) loads
-// Q and G of token n at features 32t + 8g .. +7 (t = 0 .. D/32-1), which is both
-// its B-operand slice for k-step t and, by the fragment row order above, the
-// feature slice of its output values -- so Q, G and O each move as 16-byte
-// accesses with no shuffles.
+// 16 bytes of Q and of G of token n per run: features 32u + 8g .. +7 (bf16) or
+// 64u + 16g .. +15 (fp8, two k-steps). That is both its B-operand slice and, by
+// the fragment order (frag_pos), the feature run of its output values -- so Q,
+// G and O each move as 16-byte accesses with no shuffles.
 template <int D, bool OUT_F32, typename TIn>
 __global__ __launch_bounds__(256, 2) void linear_out_bf16(const TIn* __restrict__ Q,
                                                        const TIn* __restrict__ G,
                                                        void* __restrict__ out,
                                                        const uint32_t* __restrict__ state, int N,
                                                        float eps, int accumulate) {
+  constexpr bool F8 = sizeof(TIn) == 1;
   constexpr int NT = D / 32, NJ = D / 16, NF = (NJ + 1) * NT;
+  constexpr int EPL = 16 / sizeof(TIn);  // features per run
+  constexpr int NU = D / 4 / EPL;        // runs per lane and token
+  constexpr int JPU = NJ / NU;           // output fragments per run
   __shared__ u32x4 fr[NF * 64];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -268,24 +311,24 @@ __global__ __launch_bounds__(256, 2) void linear_out_bf16(const TIn* __restrict_
   int grp = blockIdx.x * 4 + wave;
   if (grp * 16 >= N) return;
 
-  u32x4 qv[NT], gv[NT];
+  u32x4 qv[NU], gv[NU];  // raw bytes as loaded
   auto load = [&](int gi, u32x4* qd, u32x4* gd) {
     const int tok = gi * 16 + n;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
+    for (int u = 0; u < NU; ++u) {
       if (tok < N) {
-        qd[t] = load8_bf16(Qh + (size_t)tok * D + 32 * t + 8 * g);
-        gd[t] = load8_bf16(Gh + (size_t)tok * D + 32 * t + 8 * g);
+        qd[u] = ldg16(Qh + (size_t)tok * D + 4 * EPL * u + EPL * g);
+        gd[u] = ldg16(Gh + (size_t)tok * D + 4 * EPL * u + EPL * g);
       } else {
-        qd[t] = (u32x4){0, 0, 0, 0};
-        gd[t] = (u32x4){0, 0, 0, 0};
+        qd[u] = (u32x4){0, 0, 0, 0};
+        gd[u] = (u32x4){0, 0, 0, 0};
       }
     }
   };
   load(grp, qv, gv);
 
   for (; grp * 16 < N; grp += stride) {
-    u32x4 qn[NT], gn[NT];
+    u32x4 qn[NU], gn[NU];
     const bool more = (grp + stride) * 16 < N;
     if (more) load(grp + stride, qn, gn);
 
@@ -299,7 +342,7 @@ __global__ __launch_bounds__(256, 2) void linear_out_bf16(const TIn* __restrict_
     for (int j = 0; j < NJ; ++j) acc[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const u32x4 b = relu_bf16x8(qv[t]);
+      const u32x4 b = relu_bf16x8(F8 ? fp8_half(qv[t >> 1], t & 1) : qv[t]);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) acc[j] = mfma16x16x32(fr[(j * NT + t) * 64 + fo], b, acc[j]);
       accd = mfma16x16x32(fr[(NJ * NT + t) * 64 + fo], b, accd);
@@ -310,49 +353,62 @@ __global__ __launch_bounds__(256, 2) void linear_out_bf16(const TIn* __restrict_
     const int tok = grp * 16 + n;
     if (tok < N) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        float o[8];
+      for (int u = 0; u < NU; ++u) {
+        // run u: fragments JPU*u .. +JPU-1, 4 consecutive features each
+        float o[EPL], gf[EPL];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          o[e] = acc[2 * t][e];
-          o[4 + e] = acc[2 * t + 1][e];
+        for (int jj = 0; jj < JPU; ++jj)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[4 * jj + e] = acc[JPU * u + jj][e];
+        if constexpr (F8) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4 f = fp8x4_to_f32(gv[u][q]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) gf[4 * q + e] = f[e];
+          }
+        } else {
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            gf[2 * p] = bf_lo(gv[u][p]);
+            gf[2 * p + 1] = bf_hi(gv[u][p]);
+          }
         }
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          o[2 * p] = sigmoid(bf_lo(gv[t][p])) * (o[2 * p] * rden);
-          o[2 * p + 1] = sigmoid(bf_hi(gv[t][p])) * (o[2 * p + 1] * rden);
-        }
-        const size_t off = base + (size_t)tok * D + 32 * t + 8 * g;
+        for (int e = 0; e < EPL; ++e) o[e] = sigmoid(gf[e]) * (o[e] * rden);
+        const size_t off = base + (size_t)tok * D + 4 * EPL * u + EPL * g;
         if (OUT_F32) {
           float* dst = reinterpret_cast<float*>(out) + off;
-          f32x4 lo = (f32x4){o[0], o[1], o[2], o[3]};
-          f32x4 hi = (f32x4){o[4], o[5], o[6], o[7]};
-          if (accumulate) {
-            lo += *reinterpret_cast<const f32x4*>(dst);
-            hi += *reinterpret_cast<const f32x4*>(dst + 4);
+#pragma unroll
+          for (int x = 0; x < EPL / 4; ++x) {
+            f32x4 v = (f32x4){o[4 * x], o[4 * x + 1], o[4 * x + 2], o[4 * x + 3]};
+            if (accumulate) v += *reinterpret_cast<const f32x4*>(dst + 4 * x);
+            *reinterpret_cast<f32x4*>(dst + 4 * x) = v;
           }
-          *reinterpret_cast<f32x4*>(dst) = lo;
-          *reinterpret_cast<f32x4*>(dst + 4) = hi;
         } else {
           uint16_t* dst = reinterpret_cast<uint16_t*>(out) + off;
-          if (accumulate) {
-            const u32x4 prev = ldg16(dst);
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-              o[2 * p] += bf_lo(prev[p]);
-              o[2 * p + 1] += bf_hi(prev[p]);
+          for (int x = 0; x < EPL / 8; ++x) {
+            if (accumulate) {
+              const u32x4 prev = ldg16(dst + 8 * x);
+#pragma unroll
+              for (int p = 0; p < 4; ++p) {
+                o[8 * x + 2 * p] += bf_lo(prev[p]);
+                o[8 * x + 2 * p + 1] += bf_hi(prev[p]);
+              }
             }
+            stg16(dst + 8 * x, (u32x4){pack_bf16(o[8 * x], o[8 * x + 1]), pack_bf16(o[8 * x + 2], o[8 * x + 3]),
+                                       pack_bf16(o[8 * x + 4], o[8 * x + 5]),
+                                       pack_bf16(o[8 * x + 6], o[8 * x + 7])});
           }
-          stg16(dst, (u32x4){pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]), pack_bf16(o[4], o[5]),
-                             pack_bf16(o[6], o[7])});
         }
       }
     }
     if (more) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        qv[t] = qn[t];
-        gv[t] = gn[t];
+      for (int u = 0; u < NU; ++u) {
+        qv[u] = qn[u];
+        gv[u] = gn[u];
       }
     }
   }
@@ -376,8 +432,8 @@ hipError_t launch_d(const hla_dims& d, const void* q, const void* k, const void*
   else
     hipLaunchKernelGGL((linear_state_bf16<D, false, TIn>), dim3(plan.C, BH), dim3(256), 0, stream,
                        Kp, Vp, nullptr, part, N, plan.T, plan.C);
-  hipLaunchKernelGGL(linear_reduce_bf16<D>, dim3(D * D / 8 / 256 + 1, BH), dim3(256), 0, stream,
-                     part, state, plan.C);
+  hipLaunchKernelGGL((linear_reduce_bf16<D, sizeof(TIn) == 1>), dim3(D * D / 8 / 256 + 1, BH),
+                     dim3(256), 0, stream, part, state, plan.C);
   if (d.out_dtype == HLA_F32)
     hipLaunchKernelGGL((linear_out_bf16<D, true, TIn>), dim3(plan.P, BH), dim3(256), 0, stream,
                        Qp, Gp, out, state, N, eps, accumulate);

@@ -23,6 +23,14 @@ The pages give no formula for either operator. The readings used here are:
   stack  : x_l = x_{l-1} + layer_l(Q_l, K_l, V_l, G_l), kinds L,L,L,S repeating
   write  : linear attention whose state takes beta_m = sigma(W_m) of each token's
            phi(K_m) (in S and in z), W one logit per token and head
+  attnres: blocks of 8 layers; the summary of a completed block is its total
+           update of the residual stream, s_i = x_end - x_start; a linear layer
+           in a later block reads x + sum_i alpha_i s_i with, per token,
+           alpha = softmax_i((x W) . s_i / sqrt(D)) and one router projection W
+           shared by every layer (ai-papers.net summary, section on attention
+           residuals: 8-layer blocks, block summaries routed to later linear
+           layers, a depth-shared query router; lode.cx article and SANA-Video 2.0
+           abstract: completed block summaries into later linear layers)
 Every array is float64; bf16 or fp32 inputs are upcast exactly.
 """
 from __future__ import annotations
@@ -176,6 +184,40 @@ def hybrid_stack(x0, layers, kinds, eps: float, scale: float):
     for kind, (q, k, v, g) in zip(kinds, layers):
         x = x + layer(kind, q, k, v, g, eps, scale)
     return x
+
+
+# ----------------------------------------------------------------------------
+# block attention residuals (AttnRes)
+# ----------------------------------------------------------------------------
+
+ATTNRES_BLOCK = 8  # layers per block
+
+
+def block_summary(x_start, x_end):
+    """Summary of a completed block: what it added to the residual stream."""
+    return as_f64(x_end) - as_f64(x_start)
+
+
+def attnres_route(x, summaries, w):
+    """Residual stream a later linear layer reads: x + sum_i alpha_i s_i.
+
+    x: [..., N, D]; summaries: sequence of M arrays shaped like x (completed
+    blocks, in any order); w: [D, D], the router projection shared across depth.
+    Per token n: q = x_n W, a_i = q . s_i,n / sqrt(D), alpha = softmax over the
+    M blocks. With no completed block the stream passes unchanged.
+    """
+    x = as_f64(x)
+    if len(summaries) == 0:
+        return x.copy()
+    W = as_f64(w)
+    D = x.shape[-1]
+    S = np.stack([as_f64(si) for si in summaries])     # [M, ..., N, D]
+    q = x @ W                                          # [..., N, D]
+    a = (q[None] * S).sum(-1) / np.sqrt(D)             # [M, ..., N]
+    a = a - a.max(axis=0, keepdims=True)
+    e = np.exp(a)
+    alpha = e / e.sum(axis=0, keepdims=True)
+    return x + (alpha[..., None] * S).sum(0)
 
 
 # ----------------------------------------------------------------------------

@@ -211,3 +211,65 @@ def test_correct_write_gated_oracle_passes_checks():
 @pytest.mark.parametrize("mutant", [wl_state_only, wl_norm_only, wl_on_queries, wl_no_sigmoid])
 def test_write_gated_mutant_is_caught(mutant):
     assert write_checks(mutant) > 0, mutant.__name__
+
+
+# --- block attention residual (routing) mutants -----------------------------
+
+from tests.test_oracle_pins import brute_attnres  # noqa: E402
+
+
+def _route(x, S, w, q_of=lambda x, w: x @ w, scale=True, axis=0, residual=True):
+    D = x.shape[-1]
+    St = np.stack(S)
+    a = (q_of(x, w)[None] * St).sum(-1) / (np.sqrt(D) if scale else 1.0)
+    a = a - a.max(axis=axis, keepdims=True)
+    e = np.exp(a)
+    al = e / e.sum(axis=axis, keepdims=True)
+    r = (al[..., None] * St).sum(0)
+    return x + r if residual else r
+
+
+def ar_no_scale(x, S, w):
+    return _route(x, S, w, scale=False)
+
+
+def ar_router_transposed(x, S, w):
+    return _route(x, S, w, q_of=lambda x, w: x @ w.T)
+
+
+def ar_no_projection(x, S, w):
+    return _route(x, S, w, q_of=lambda x, w: x)
+
+
+def ar_softmax_over_tokens(x, S, w):
+    return _route(x, S, w, axis=1)
+
+
+def ar_no_residual(x, S, w):
+    return _route(x, S, w, residual=False)
+
+
+def attnres_checks(f):
+    fails = 0
+    for (N, D, M, seed) in [(6, 4, 3, 1), (9, 8, 2, 2)]:
+        x = rand((N, D), 800 + seed * 10)
+        w = rand((D, D), 801 + seed * 10, scale=0.7)
+        S = [rand((N, D), 802 + seed * 10 + i) for i in range(M)]
+        try:
+            got = f(x, S, w)
+            ref = np.array(brute_attnres(x.tolist(), [s.tolist() for s in S], w.tolist()))
+            if got.shape != ref.shape or not np.allclose(got, ref, rtol=1e-10, atol=1e-12):
+                fails += 1
+        except Exception:
+            fails += 1
+    return fails
+
+
+def test_correct_attnres_oracle_passes_checks():
+    assert attnres_checks(oracle.attnres_route) == 0
+
+
+@pytest.mark.parametrize("mutant", [ar_no_scale, ar_router_transposed, ar_no_projection,
+                                     ar_softmax_over_tokens, ar_no_residual])
+def test_attnres_mutant_is_caught(mutant):
+    assert attnres_checks(mutant) > 0

@@ -426,3 +426,79 @@ def test_write_gated_quadratic_closed_form():
     A = np.maximum(q, 0) @ (beta[..., :, None] * np.maximum(k, 0)).swapaxes(-1, -2)
     ref = (1 / (1 + np.exp(-g))) * (A @ v) / (A.sum(axis=-1, keepdims=True) + 1e-6)
     assert _close(oracle.gated_linear_write(q, k, v, g, w, 1e-6), ref, tol=1e-11)
+
+
+# ----------------------------------------------------------------------------
+# block attention residuals: routing completed block summaries
+# ----------------------------------------------------------------------------
+
+def brute_attnres(x, summaries, w):
+    """Per token n: q_j = sum_k x_k W[k][j]; a_i = sum_j q_j s_i[j] / sqrt(D);
+    alpha = softmax over the blocks i; returns x + sum_i alpha_i s_i."""
+    N, D, M = len(x), len(x[0]), len(summaries)
+    out = []
+    for n in range(N):
+        q = [sum(x[n][k] * w[k][j] for k in range(D)) for j in range(D)]
+        a = [sum(q[j] * summaries[i][n][j] for j in range(D)) / math.sqrt(D) for i in range(M)]
+        top = max(a)
+        e = [math.exp(ai - top) for ai in a]
+        tot = sum(e)
+        out.append([x[n][j] + sum(e[i] / tot * summaries[i][n][j] for i in range(M))
+                    for j in range(D)])
+    return out
+
+
+@pytest.mark.parametrize("N,D,M", [(1, 4, 1), (5, 6, 3), (12, 16, 4)])
+def test_attnres_route_matches_brute_force(N, D, M):
+    x = rand((N, D), seed=90)
+    w = rand((D, D), seed=91, scale=0.5)
+    S = [rand((N, D), seed=92 + i) for i in range(M)]
+    ref = brute_attnres(x.tolist(), [s.tolist() for s in S], w.tolist())
+    assert _close(oracle.attnres_route(x, S, w), ref)
+
+
+def test_attnres_one_block_adds_its_summary():
+    # a single completed block gets weight 1 whatever the router computes
+    x, s = rand((2, 3, 20, 8), seed=100), rand((2, 3, 20, 8), seed=101)
+    w = rand((8, 8), seed=102, scale=5.0)
+    assert _close(oracle.attnres_route(x, [s], w), x + s, tol=1e-15)
+
+
+def test_attnres_zero_router_averages_the_blocks():
+    x = rand((1, 2, 15, 8), seed=110)
+    S = [rand((1, 2, 15, 8), seed=111 + i) for i in range(3)]
+    assert _close(oracle.attnres_route(x, S, np.zeros((8, 8))), x + sum(S) / 3, tol=1e-14)
+
+
+def test_attnres_block_order_and_identical_blocks():
+    x = rand((1, 1, 25, 8), seed=120)
+    S = [rand((1, 1, 25, 8), seed=121 + i) for i in range(4)]
+    w = rand((8, 8), seed=125)
+    assert _close(oracle.attnres_route(x, S, w), oracle.attnres_route(x, S[::-1], w), tol=1e-14)
+    assert _close(oracle.attnres_route(x, [S[0]] * 3, w), x + S[0], tol=1e-14)
+
+
+def test_attnres_no_completed_block_passes_the_stream():
+    x = rand((1, 2, 7, 8), seed=130)
+    out = oracle.attnres_route(x, [], np.eye(8))
+    assert np.array_equal(out, x)
+
+
+def test_attnres_dominant_block_is_selected():
+    # W = 100 I makes q = 100 x; a block equal to x scores 100|x|^2/sqrt(D), one
+    # equal to -x the negative: the gap is hundreds, so softmax is one-hot in fp64
+    x = rand((1, 1, 10, 8), seed=140) + 2.0
+    out = oracle.attnres_route(x, [-x, x], 100.0 * np.eye(8))
+    assert _close(out, 2.0 * x, tol=1e-15)
+
+
+def test_block_summary_is_the_blocks_layer_sum():
+    # the summary of one 8-layer block (3:1 kinds) equals the sum of its layers' outputs
+    B, H, N, D = 1, 1, 12, 4
+    kinds = oracle.hybrid_kinds(oracle.ATTNRES_BLOCK)
+    layers = [tuple(rand((B, H, N, D), seed=150 + 4 * l + i) for i in range(4)) for l in range(8)]
+    x0 = rand((B, H, N, D), seed=190)
+    x8 = oracle.hybrid_stack(x0, layers, kinds, 1e-6, D ** -0.5)
+    ref = [brute_linear(*(t[0, 0].tolist() for t in L), 1e-6) if kd == oracle.LINEAR else
+           brute_softmax(*(t[0, 0].tolist() for t in L), D ** -0.5) for kd, L in zip(kinds, layers)]
+    assert _close(oracle.block_summary(x0, x8)[0, 0], np.sum(np.array(ref), axis=0), tol=1e-12)

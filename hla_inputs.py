@@ -22,7 +22,7 @@ import torch
 
 SEED_BASE = 20261203
 # tensor slot inside a layer's seed: q, k, v, g, and the residual stream x0
-SLOT = {"q": 0, "k": 1, "v": 2, "g": 3, "x0": 4}
+SLOT = {"q": 0, "k": 1, "v": 2, "g": 3, "x0": 4, "summary": 5, "router": 6}
 
 LINEAR = 0
 SOFTMAX = 1
@@ -124,6 +124,24 @@ def residual_x0(w: Workload, B: int = None, H: int = None, N: int = None) -> tor
     H = w.H if H is None else H
     N = w.N if N is None else N
     return randn((B, H, N, w.D), seed_for(w.index, 0, "x0"), torch.float32)
+
+
+def attnres_inputs(w: Workload, n_blocks: int, B: int = None, H: int = None, N: int = None):
+    """(x, summaries, router) for the block-attention-residual routing.
+
+    x and the ``n_blocks`` block summaries are fp32 [B, H, N, D], N(0, 1) (a block
+    summary is a sum of layer outputs of about unit size); the router W is bf16
+    [D, D] with N(0, 4/D) entries, so q = x W has entries of about 2 and the
+    per-token scores q . s / sqrt(D) spread over a few units.
+    """
+    B = w.B if B is None else B
+    H = w.H if H is None else H
+    N = w.N if N is None else N
+    shape = (B, H, N, w.D)
+    x = randn(shape, seed_for(w.index, 0, "x0"), torch.float32)
+    summaries = [randn(shape, seed_for(w.index, i, "summary"), torch.float32) for i in range(n_blocks)]
+    router = (randn((w.D, w.D), seed_for(w.index, 0, "router"), torch.float32) * (2.0 / w.D ** 0.5))
+    return x, summaries, router.to(torch.bfloat16)
 
 
 def custom(shape, seed: int, dtype: torch.dtype = torch.float32, n: int = 4):

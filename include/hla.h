@@ -152,6 +152,28 @@ hla_status hla_hybrid_stack_fwd(const hla_dims* d, int n_layers, const int32_t* 
                                 float scale, void* workspace, size_t workspace_bytes,
                                 void* stream);
 
+/* Block attention residuals (AttnRes) routing -- SANA-Video 2.0 groups layers into
+ * blocks of 8 and routes a summary of every completed block directly into later
+ * linear layers through a query router shared across depth (ai-papers.net summary,
+ * section on attention residuals; lode.cx article, "The Core Innovation"; SANA-Video
+ * 2.0 abstract). The pages give no formula; this is one reading of it. Per token n
+ * of each (b, h):
+ *   q_n = x_n W,  a_i = q_n . s_i,n / sqrt(D),  out_n = x_n + sum_i softmax_i(a)_i s_i,n
+ * where s_0 .. s_{n_blocks-1} are the summaries of the completed blocks (a block's
+ * summary is its total update of the residual stream, x at its end minus x at its
+ * start) and W is the router projection shared by every layer. out is the stream a
+ * later linear layer's projections read.
+ * dims: in_dtype = out_dtype = HLA_F32 (x, every summary and out: fp32
+ * [B, H, N, D]), D in {64, 128}; otherwise HLA_ERR_UNSUPPORTED. `summaries` is a
+ * HOST array of n_blocks DEVICE pointers, 0 <= n_blocks <= 16 (else HLA_ERR_BAD_ARG);
+ * w_router is a DEVICE bf16 [D, D] row-major matrix (q_j = sum_k x_k W[k][j]).
+ * q is formed on the matrix cores from x split into a bf16 hi + lo pair (about 16
+ * significant bits; fp32 sums); scores, softmax and the mix are fp32. With n_blocks = 0 out = x (a copy, or nothing when
+ * out == x). out may be x itself (in place); it must not overlap a summary or W.
+ * All device pointers 16-byte aligned. No workspace. */
+hla_status hla_attnres_route_fwd(const hla_dims* d, int n_blocks, const void* const* summaries,
+                                 const void* x, const void* w_router, void* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -2,7 +2,8 @@
 
 A thin ctypes layer over the C ABI in include/hla.h, with the same names:
 ``hla_linear_fwd``, ``hla_softmax_anchor_fwd``, ``hla_hybrid_stack_fwd``,
-``hla_linear_workspace_bytes``, ``hla_status_str``, ``hla_abi_version``. It only
+``hla_linear_workspace_bytes``, ``hla_status_str``, ``hla_abi_version``,
+``hla_linear_write_gated_fwd`` and ``hla_attnres_route_fwd``. It only
 marshals arguments: torch tensors become device pointers and the current torch
 stream becomes the HIP stream; every step of the computation runs in the HIP
 kernels. The shared library must have been built (``python
@@ -29,7 +30,7 @@ STATUS = {
 }
 EXPORTS = ("hla_abi_version", "hla_status_str", "hla_linear_workspace_bytes", "hla_linear_fwd",
            "hla_linear_write_gated_fwd", "hla_softmax_anchor_workspace_bytes",
-           "hla_softmax_anchor_fwd", "hla_hybrid_stack_fwd")
+           "hla_softmax_anchor_fwd", "hla_hybrid_stack_fwd", "hla_attnres_route_fwd")
 
 
 class hla_dims(ctypes.Structure):
@@ -90,6 +91,8 @@ def _load() -> ctypes.CDLL:
                                          ctypes.POINTER(P), ctypes.POINTER(P), ctypes.POINTER(P),
                                          ctypes.POINTER(P), P, ctypes.c_float, ctypes.c_float, P,
                                          ctypes.c_size_t, P]
+    lib.hla_attnres_route_fwd.restype = ctypes.c_int
+    lib.hla_attnres_route_fwd.argtypes = [pd, ctypes.c_int, ctypes.POINTER(P), P, P, P, P]
     return lib
 
 
@@ -291,3 +294,28 @@ def hla_hybrid_stack_fwd(x, layers: Sequence, kinds: Sequence[int], eps: float =
                                   scale, wp, wb, _stream(stream))
     _raise("hla_hybrid_stack_fwd", st)
     return x
+
+
+def hla_attnres_route_fwd(x, summaries: Sequence, w, out=None, stream=None):
+    """Routed residual stream x + sum_i softmax_i((x W) . s_i / sqrt(D)) s_i; returns out.
+
+    x and every summary: fp32 [B, H, N, D] on the GPU; w: bf16 [D, D] router
+    projection shared across depth; out defaults to a new tensor (pass x to route
+    in place)."""
+    torch = _torch()
+    _check(x, *summaries)
+    if x.dtype != torch.float32 or any(s_.dtype != torch.float32 for s_ in summaries):
+        raise ValueError("x and the summaries must be fp32")
+    D = int(x.shape[-1])
+    if tuple(w.shape) != (D, D) or w.dtype != torch.bfloat16 or not w.is_contiguous() or not w.is_cuda:
+        raise ValueError("w must be a contiguous bf16 [D, D] tensor on the GPU")
+    if out is None:
+        out = torch.empty_like(x)
+    _check(x, out)
+    d = dims_of(x, out.dtype)
+    n = len(summaries)
+    arr = (ctypes.c_void_p * max(n, 1))(*[s_.data_ptr() for s_ in summaries])
+    st = lib.hla_attnres_route_fwd(ctypes.byref(d), n, arr, x.data_ptr(), w.data_ptr(),
+                                   out.data_ptr(), _stream(stream))
+    _raise("hla_attnres_route_fwd", st)
+    return out

@@ -1,0 +1,172 @@
+// Block attention residuals (AttnRes): routing the summaries of completed
+// 8-layer blocks into the residual stream a later linear layer reads.
+//
+// SANA-Video 2.0 groups consecutive layers into blocks of 8 and routes a summary
+// of each completed block directly into later linear layers, through a router
+// whose query projection is shared across depth (ai-papers.net summary, section
+// on attention residuals; lode.cx article, "The Core Innovation"; SANA-Video 2.0
+// abstract). The pages give no formula; the reading built here is, per token n
+// of one (b, h):
+//   q_n = x_n W                         (W: D x D bf16, one matrix for all layers)
+//   a_i = q_n . s_i,n / sqrt(D)         (s_i: summary of completed block i)
+//   out_n = x_n + sum_i softmax_i(a)_i s_i,n
+// x, the summaries and out are fp32 [B, H, N, D] (the residual stream).
+//
+// One pass over HBM: each wave takes 16 tokens at a time; lane (n = lane & 15,
+// g = lane >> 4) owns features 32t + 8g .. +7 (t < D/32) of token n. q comes
+// from 16x16x32 bf16 MFMAs with W^T fragments in LDS and x split into a bf16
+// hi + lo pair as the B operands (about 16 significant bits of x: the scores are
+// exponentiated, so an 8-bit x would move them by up to ~0.1 when they spread
+// over tens of units), and lands in the same lanes and features as the lane's x slice,
+// so the score of block i is the lane's partial dot product summed over the
+// four lanes of the token. The blocks are streamed once each through an online
+// softmax (running max, running sum, running weighted summary), so any number
+// of blocks costs one read of each.
+#include "hla_device.h"
+#include "hla_internal.h"
+
+namespace hla {
+namespace {
+
+// Fragment (j, t) of W^T for the 16x16x32 MFMA: A[i][k] = W[32t + k][c(j, i)] with
+// c(j, i) = 32(j>>1) + 8(i>>2) + 4(j&1) + (i&3), so output lane (n, g) ends with
+// q at features 32t + 8g + 0..7 from fragments j = 2t, 2t+1 (as its x slice).
+template <int D>
+__device__ __forceinline__ u32x4 w_fragment(const uint16_t* __restrict__ W, int j, int t, int l) {
+  const int i = l & 15, k0 = 8 * (l >> 4);
+  const int col = 32 * (j >> 1) + 8 * (i >> 2) + 4 * (j & 1) + (i & 3);
+  uint32_t w[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int row = 32 * t + k0 + 2 * p;
+    w[p] = uint32_t(W[row * D + col]) | (uint32_t(W[(row + 1) * D + col]) << 16);
+  }
+  return (u32x4){w[0], w[1], w[2], w[3]};
+}
+
+// X may be out itself (in place): no __restrict__ on either.
+template <int D>
+__global__ __launch_bounds__(256, 2) void attnres_route(const float* X,
+                                                        AttnResBlocks S, int M,
+                                                        const uint16_t* __restrict__ W,
+                                                        float* out, int N) {
+  constexpr int NT = D / 32, NJ = D / 16, NF = NJ * NT;
+  __shared__ u32x4 fr[NF * 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int x = tid; x < NF * 64; x += 256) {
+    const int f = x >> 6;
+    fr[x] = w_fragment<D>(W, f / NT, f % NT, x & 63);
+  }
+  __syncthreads();
+
+  const int bh = blockIdx.y, n = lane & 15, g = lane >> 4;
+  const size_t base = (size_t)bh * N * D;
+  const float c = kLog2e * rsqrtf((float)D);  // scores in log2 units
+  const int stride = gridDim.x * 4;
+  for (int grp = blockIdx.x * 4 + wave; grp * 16 < N; grp += stride) {
+    const int tok = grp * 16 + n;
+    const bool live = tok < N;
+    const size_t row = base + (size_t)(live ? tok : 0) * D + 8 * g;
+    // slice of a [B,H,N,D] fp32 tensor: features 32t + 8g + 0..7 of this token
+    auto load = [&](const float* T, f32x4* v) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        v[2 * t] = live ? *reinterpret_cast<const f32x4*>(T + row + 32 * t) : (f32x4){0.f, 0.f, 0.f, 0.f};
+        v[2 * t + 1] = live ? *reinterpret_cast<const f32x4*>(T + row + 32 * t + 4) : (f32x4){0.f, 0.f, 0.f, 0.f};
+      }
+    };
+    f32x4 xv[2 * NT], sv[2 * NT];
+    load(X, xv);
+    if (M > 0) load(S.p[0], sv);
+
+    // q = x W on the matrix cores. The fragments are re-read from LDS every
+    // group: an opaque (always equal) offset keeps the compiler from hoisting all
+    // of them into registers, which would spill.
+    int fo = lane;
+    asm volatile("" : "+v"(fo));
+    f32x4 acc[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      float v[8], lo[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] = xv[2 * t][e];
+        v[4 + e] = xv[2 * t + 1][e];
+      }
+      u32x4 bh, bl;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        bh[p] = pack_bf16(v[2 * p], v[2 * p + 1]);
+        lo[2 * p] = v[2 * p] - bf_lo(bh[p]);
+        lo[2 * p + 1] = v[2 * p + 1] - bf_hi(bh[p]);
+        bl[p] = pack_bf16(lo[2 * p], lo[2 * p + 1]);
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const u32x4 a = fr[(j * NT + t) * 64 + fo];
+        acc[j] = mfma16x16x32(a, bh, acc[j]);
+        acc[j] = mfma16x16x32(a, bl, acc[j]);
+      }
+    }
+
+    // online softmax over the blocks
+    float m = -INFINITY, l = 0.f;
+    f32x4 r[2 * NT];
+#pragma unroll
+    for (int x = 0; x < 2 * NT; ++x) r[x] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < M; ++i) {
+      f32x4 cur[2 * NT];
+#pragma unroll
+      for (int x = 0; x < 2 * NT; ++x) cur[x] = sv[x];
+      if (i + 1 < M) load(S.p[i + 1], sv);  // next block in flight
+      float part = 0.f;
+#pragma unroll
+      for (int x = 0; x < 2 * NT; ++x)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) part = fmaf(acc[x][e], cur[x][e], part);
+      part += __shfl_xor(part, 16);
+      part += __shfl_xor(part, 32);
+      // rounded on its own (the empty asm pins the product): a fused
+      // c * part - m_new would leave the product's rounding error where a - m_new
+      // must be exactly 0 for the largest score
+      float a = part * c;
+      asm volatile("" : "+v"(a));
+      const float m_new = fmaxf(m, a);
+      const float corr = exp2_fast(m - m_new), p = exp2_fast(a - m_new);
+      l = fmaf(l, corr, p);
+#pragma unroll
+      for (int x = 0; x < 2 * NT; ++x) r[x] = r[x] * corr + p * cur[x];
+      m = m_new;
+    }
+    if (!live) continue;
+    const float inv = M > 0 ? 1.0f / l : 0.f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      *reinterpret_cast<f32x4*>(out + row + 32 * t) = xv[2 * t] + r[2 * t] * inv;
+      *reinterpret_cast<f32x4*>(out + row + 32 * t + 4) = xv[2 * t + 1] + r[2 * t + 1] * inv;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attnres_route(const hla_dims& d, int n_blocks, const AttnResBlocks& blocks,
+                                const void* x, const void* w, void* out, hipStream_t stream) {
+  const int BH = int(d.B * d.H), N = int(d.N);
+  const int groups = (N + 15) / 16;
+  int P = (1024 + BH - 1) / BH;  // about four workgroups per CU in all
+  const int maxp = (groups + 3) / 4;
+  P = P < 1 ? 1 : (P > maxp ? maxp : P);
+  const float* X = reinterpret_cast<const float*>(x);
+  const uint16_t* W = reinterpret_cast<const uint16_t*>(w);
+  float* O = reinterpret_cast<float*>(out);
+  if (d.D == 128)
+    hipLaunchKernelGGL(attnres_route<128>, dim3(P, BH), dim3(256), 0, stream, X, blocks, n_blocks, W, O, N);
+  else
+    hipLaunchKernelGGL(attnres_route<64>, dim3(P, BH), dim3(256), 0, stream, X, blocks, n_blocks, W, O, N);
+  return hipGetLastError();
+}
+
+}  // namespace hla

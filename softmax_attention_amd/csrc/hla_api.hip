@@ -244,4 +244,35 @@ hla_status hla_hybrid_stack_fwd(const hla_dims* d, int n_layers, const int32_t* 
   return HLA_OK;
 }
 
+hla_status hla_attnres_route_fwd(const hla_dims* d, int n_blocks, const void* const* summaries,
+                                 const void* x, const void* w_router, void* out, void* stream) {
+  hla_status st = check_dims(d);
+  if (st != HLA_OK) return st;
+  if (d->in_dtype != HLA_F32 || d->out_dtype != HLA_F32 || (d->D != 64 && d->D != 128))
+    return HLA_ERR_UNSUPPORTED;
+  if (n_blocks < 0 || n_blocks > kMaxAttnResBlocks) return HLA_ERR_BAD_ARG;
+  if (n_blocks > 0 && !summaries) return HLA_ERR_NULL_PTR;
+  if (empty(d)) return HLA_OK;
+  if (!x || !out) return HLA_ERR_NULL_PTR;
+  if (!aligned16(x) || !aligned16(out)) return HLA_ERR_ALIGN;
+  AttnResBlocks blocks{};
+  if (n_blocks > 0) {
+    if (!w_router) return HLA_ERR_NULL_PTR;
+    if (!aligned16(w_router)) return HLA_ERR_ALIGN;
+    for (int i = 0; i < n_blocks; ++i) {
+      if (!summaries[i]) return HLA_ERR_NULL_PTR;
+      if (!aligned16(summaries[i])) return HLA_ERR_ALIGN;
+      blocks.p[i] = reinterpret_cast<const float*>(summaries[i]);
+    }
+  }
+  if (n_blocks == 0 && out == x) return HLA_OK;  // no completed block, in place: nothing to do
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  clear_pending_error();
+  if (n_blocks == 0) {  // no completed block: the stream passes unchanged
+    const size_t bytes = size_t(d->B * d->H * d->N * d->D) * 4;
+    return from_hip(hipMemcpyAsync(out, x, bytes, hipMemcpyDeviceToDevice, s));
+  }
+  return from_hip(launch_attnres_route(*d, n_blocks, blocks, x, w_router, out, s));
+}
+
 }  // extern "C"

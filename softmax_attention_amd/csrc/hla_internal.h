@@ -45,6 +45,15 @@ hipError_t launch_anchor_f32(const hla_dims& d, const void* q, const void* k, co
                              const void* g, void* out, int accumulate, float scale,
                              hipStream_t stream);
 
+// Block summaries of the attention-residual routing, passed to the kernel by value.
+constexpr int kMaxAttnResBlocks = 16;
+struct AttnResBlocks {
+  const float* p[kMaxAttnResBlocks];
+};
+// x, summaries, out: fp32 [B,H,N,D]; w: bf16 [D,D]; 1 <= n_blocks <= kMaxAttnResBlocks
+hipError_t launch_attnres_route(const hla_dims& d, int n_blocks, const AttnResBlocks& blocks,
+                                const void* x, const void* w, void* out, hipStream_t stream);
+
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace hla

@@ -58,6 +58,13 @@ def stack(d, n=2, kinds=(0, 1), ptrs=None, x=FAKE, eps=1e-6, scale=0.1, ws=FAKE,
                                         q, x, eps, scale, ws, wsb, None)
 
 
+def route(d, n=2, ptrs=None, x=FAKE, w=FAKE, out=FAKE):
+    arr = ctypes.c_void_p * max(n, 1)
+    p = ptrs if ptrs is not None else [FAKE] * max(n, 1)
+    return hla.lib.hla_attnres_route_fwd(ctypes.byref(d) if d is not None else None, n, arr(*p), x, w,
+                                         out, None)
+
+
 def test_header_declares_the_abi():
     fns = declared_functions()
     assert fns == sorted(hla.EXPORTS)
@@ -215,6 +222,29 @@ def test_stack_argument_errors():
     assert stack(d, kinds=(1, 1), wsb=hla.hla_softmax_anchor_workspace_bytes(d) - 16) == WS
     assert stack(dims(D=40, o=F32)) == UNSUP
     assert stack(dims(N=-1, o=F32)) == SHAPE
+
+
+def test_attnres_argument_errors():
+    d = dims(i=F32, o=F32)
+    assert route(None) == NULLP
+    assert route(dims(i=BF16, o=BF16)) == UNSUP        # the residual stream is fp32
+    assert route(dims(i=BF16, o=F32)) == UNSUP
+    assert route(dims(i=FP8, o=F32)) == UNSUP
+    assert route(dims(i=F32, o=F32, D=32)) == UNSUP     # D in {64, 128}
+    assert route(dims(i=F32, o=F32, D=96)) == UNSUP
+    assert route(dims(i=F32, o=F32, N=-1)) == SHAPE
+    assert route(d, n=-1) == BADARG
+    assert route(d, n=17, ptrs=[FAKE] * 17) == BADARG
+    assert hla.lib.hla_attnres_route_fwd(ctypes.byref(d), 2, None, FAKE, FAKE, FAKE, None) == NULLP
+    for p in ("x", "w", "out"):
+        assert route(d, **{p: None}) == NULLP, p
+        assert route(d, **{p: ODD}) == ALIGN, p
+    assert route(d, ptrs=[FAKE, None]) == NULLP
+    assert route(d, ptrs=[FAKE, ODD]) == ALIGN
+    # empty tensors: valid, nothing to do, pointers may be NULL
+    assert route(dims(i=F32, o=F32, N=0), x=None, w=None, out=None) == OK
+    # no completed block, in place: the stream passes unchanged, W is not needed
+    assert route(d, n=0, ptrs=[], w=None) == OK
 
 
 def test_empty_tensors_are_a_no_op():

@@ -15,7 +15,8 @@ stack).
 --profile {anchor,linear,step,copy} runs just that piece a few times, for
 rocprofv3 kernel traces and counter passes (copy: a plain device copy of known
 size that calibrates FETCH_SIZE / WRITE_SIZE); anchor_fp8, linear_fp8 and
-step_fp8 do the same on fp8 (e4m3) copies of the inputs.
+step_fp8 do the same on fp8 (e4m3) copies of the inputs; attnres runs the
+block-attention-residual routing at the stack shape with two blocks.
 """
 from __future__ import annotations
 
@@ -86,7 +87,8 @@ def parse():
     ap.add_argument("--no-stack", action="store_true", help="skip the hybrid-stack detail timing")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--profile", default=None,
-                    choices=["anchor", "linear", "step", "copy", "anchor_fp8", "linear_fp8", "step_fp8"])
+                    choices=["anchor", "linear", "step", "copy", "anchor_fp8", "linear_fp8", "step_fp8",
+                             "attnres"])
     ap.add_argument("--iters", type=int, default=5, help="launches per --profile run")
     ap.add_argument("--sweep", action="store_true",
                     help="720p duration sweep: one gated linear and one gated softmax layer per clip "
@@ -160,6 +162,13 @@ def main():
 
     if args.sweep:
         duration_sweep(torch, hla)
+        return
+
+    if args.profile == "attnres":
+        for _ in range(args.warmup):
+            attnres_timing(torch, hla, reps=1)
+        res = attnres_timing(torch, hla, reps=args.iters)
+        print(json.dumps({"profile": "attnres", **res}))
         return
 
     if args.profile == "copy":

@@ -120,16 +120,6 @@ __device__ __forceinline__ void buf_load16_lds(rsrc_t r, uint32_t byte_off, void
 // Wait until every outstanding memory operation of this wave has completed.
 __device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
 
-// LDS transpose read (ds_read_b64_tr_b16): within each group of 16 lanes, lane j
-// receives element (j % 4) of the 8-byte rows that lanes 4e + j/4 (e = 0..3)
-// point at, as its elements e = 0..3.
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* lds_elem) {
-  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_elem));
-  return __builtin_bit_cast(u32x2, v);
-}
-
 // Row sum helper: a + lo(p) + hi(p) for a packed bf16 pair p (v_dot2 with ones).
 __device__ __forceinline__ float add_bf16x2(uint32_t p, float a) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p),

@@ -392,32 +392,40 @@ def test_write_gated_full_720p():
 def test_graph_capture_replays_match_eager():
     # the calls enqueue kernels only (no allocation, no memset), so they can be
     # captured in a HIP graph; every replay must reproduce the eager result
+    # (linear, anchor, write-gated linear and the block-summary routing)
     B, H, N, D = 1, 4, 1500, 128
     q, k, v, g = (t.to(DEV) for t in make((B, H, N, D), 9000, torch.bfloat16))
     w = wlogits((B, H, N), 9100, torch.bfloat16).to(DEV)
+    x, s0, s1 = (t.to(DEV) for t in custom((B, H, N, D), 9200, torch.float32, n=3))
+    router = (custom((D, D), 9300, torch.float32, n=1)[0] * (2.0 / D ** 0.5)).to(torch.bfloat16).to(DEV)
     ws_l, ws_a = hla.linear_workspace(q), hla.anchor_workspace(q)
     out_l, out_a, out_w = (torch.empty_like(q) for _ in range(3))
+    out_r = torch.empty_like(x)
+
+    def calls():
+        hla.hla_linear_fwd(q, k, v, g, out=out_l, workspace=ws_l)
+        hla.hla_softmax_anchor_fwd(q, k, v, g, out=out_a, workspace=ws_a)
+        hla.hla_linear_write_gated_fwd(q, k, v, g, w, out=out_w, workspace=ws_l)
+        hla.hla_attnres_route_fwd(x, [s0, s1], router, out=out_r)
+
+    outs = (out_l, out_a, out_w, out_r)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        hla.hla_linear_fwd(q, k, v, g, out=out_l, workspace=ws_l)
-        hla.hla_softmax_anchor_fwd(q, k, v, g, out=out_a, workspace=ws_a)
-        hla.hla_linear_write_gated_fwd(q, k, v, g, w, out=out_w, workspace=ws_l)
+        calls()
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
-    eager = [t.clone() for t in (out_l, out_a, out_w)]
+    eager = [t.clone() for t in outs]
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        hla.hla_linear_fwd(q, k, v, g, out=out_l, workspace=ws_l)
-        hla.hla_softmax_anchor_fwd(q, k, v, g, out=out_a, workspace=ws_a)
-        hla.hla_linear_write_gated_fwd(q, k, v, g, w, out=out_w, workspace=ws_l)
+        calls()
     for rep in range(3):
-        for t in (out_l, out_a, out_w):
+        for t in outs:
             t.zero_()
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        for got, ref in zip((out_l, out_a, out_w), eager):
+        for got, ref in zip(outs, eager):
             assert torch.equal(got, ref), rep
 
 

@@ -78,18 +78,27 @@ def linear_state(k, v):
     return S, z
 
 
+def linear_readout(q, g, S, z, eps: float):
+    """Output rows of gated linear attention from its state (S, z).
+
+    O_n = sigma(G_n) * (phi(Q_n) S) / (phi(Q_n) . z + eps); q, g: [..., R, D] (any
+    R rows), S: [..., D, D], z: [..., D].
+    """
+    q = as_f64(q)
+    g = as_f64(g)
+    phq = relu(q)
+    num = np.matmul(phq, as_f64(S))
+    den = np.matmul(phq, as_f64(z)[..., :, None])[..., 0] + float(eps)
+    return sigmoid(g) * num / den[..., None]
+
+
 def gated_linear(q, k, v, g, eps: float):
     """Gated linear attention output O [..., N, D] in its O(N) (state) form.
 
     O_n = sigma(G_n) * (phi(Q_n) S) / (phi(Q_n) . z + eps)
     """
-    q = as_f64(q)
-    g = as_f64(g)
     S, z = linear_state(k, v)
-    phq = relu(q)
-    num = np.matmul(phq, S)
-    den = np.matmul(phq, z[..., :, None])[..., 0] + float(eps)
-    return sigmoid(g) * num / den[..., None]
+    return linear_readout(q, g, S, z, eps)
 
 
 def gated_linear_write(q, k, v, g, w, eps: float):

@@ -558,3 +558,29 @@ def test_softmax_fp8_full_720p_sampled():
     e = rel_err(sm[..., rows, :], oracle.gated_softmax(q, k, v, g, w.scale, rows=rows))
     print(f"[720p_81f fp8] softmax err {e:.3e} on {len(rows)} rows", flush=True)
     assert e <= TOL[torch.bfloat16]
+
+
+def test_linear_beyond_2gib_per_tensor():
+    # one head whose bf16 tensors exceed 2^31 bytes (N*D*2 = 2.15 GB): every byte
+    # offset past the 32-bit signed range must still land right. Reference: the
+    # state summed over token chunks in fp64, read out on sampled rows.
+    from hla_inputs import randn
+    N, D = 8_400_001, 128
+    shape = (1, 1, N, D)
+    print(f"[max-size linear] N={N} D={D} ({N * D * 2 / 2**30:.2f} GiB per tensor)", flush=True)
+    q, k, v, g = (randn(shape, 12000 + i, torch.bfloat16) for i in range(4))
+    out = run_linear(q, k, v, g)
+    S = np.zeros((1, 1, D, D))
+    z = np.zeros((1, 1, D))
+    step = 1 << 20
+    for a in range(0, N, step):
+        Sc, zc = oracle.linear_state(k[..., a:a + step, :], v[..., a:a + step, :])
+        S += Sc
+        z += zc
+    rows = sample_rows(N, count=64, seed=12)
+    rows = np.unique(np.concatenate([rows, [N // 2, (1 << 23) - 1, 1 << 23, N - 3]]))  # 2^23 rows = 2^31 bytes
+    rows = rows[rows < N]
+    ref = oracle.linear_readout(q[..., rows, :], g[..., rows, :], S, z, 1e-6)
+    e = rel_err(out[..., rows, :], ref)
+    print(f"[max-size linear] err {e:.3e} on {len(rows)} rows", flush=True)
+    assert e <= TOL[torch.bfloat16]

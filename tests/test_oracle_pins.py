@@ -502,3 +502,17 @@ def test_block_summary_is_the_blocks_layer_sum():
     ref = [brute_linear(*(t[0, 0].tolist() for t in L), 1e-6) if kd == oracle.LINEAR else
            brute_softmax(*(t[0, 0].tolist() for t in L), D ** -0.5) for kd, L in zip(kinds, layers)]
     assert _close(oracle.block_summary(x0, x8)[0, 0], np.sum(np.array(ref), axis=0), tol=1e-12)
+
+
+def test_linear_state_adds_over_token_chunks():
+    # the state is a sum over tokens: chunked sums reproduce it (the large-N GPU
+    # test builds its reference this way)
+    k, v = rand((1, 2, 1000, 8), seed=200), rand((1, 2, 1000, 8), seed=201)
+    S, z = oracle.linear_state(k, v)
+    parts = [oracle.linear_state(k[..., a:a + 300, :], v[..., a:a + 300, :]) for a in range(0, 1000, 300)]
+    assert _close(sum(p[0] for p in parts), S, tol=1e-13)
+    assert _close(sum(p[1] for p in parts), z, tol=1e-13)
+    q, g = rand((1, 2, 1000, 8), seed=202), rand((1, 2, 1000, 8), seed=203)
+    rows = [0, 17, 999]
+    assert _close(oracle.linear_readout(q[..., rows, :], g[..., rows, :], S, z, 1e-6),
+                  oracle.gated_linear(q, k, v, g, 1e-6)[..., rows, :], tol=1e-14)

@@ -65,15 +65,45 @@ __device__ __forceinline__ int z_run(int t, int kg) {
 // ---------------------------------------------------------------------------
 // 1. state pass
 // ---------------------------------------------------------------------------
+// Both MFMA operands have tokens along k: A = phi(K)^T (rows = features) and
+// B = V (cols = features), each lane holding 8 consecutive tokens of one
+// feature. So the tiles are stored feature-major in LDS: each thread loads an
+// 8-token x 8-feature block (8 coalesced 16-byte loads, one per token row),
+// transposes it in registers with byte permutes and writes 8 feature rows of 8
+// tokens, and every operand is then one 16-byte LDS read. Threads 0-127 take K
+// blocks (ReLU, the write gate and the normaliser z on the way), 128-255 V
+// blocks; a tile of TILE tokens holds exactly 128 blocks per tensor.
 // Wave w owns a (D/2 x D/2) quadrant of S: 32-row blocks [(w>>1)*RB, +RB) and
-// 32-column blocks [(w&1)*RB, +RB). MFMA operand A is phi(K)^T (rows = features,
-// k = tokens) and B is V (k = tokens, cols = features); both read 8 tokens of one
-// feature per lane out of a row-major bf16 LDS tile.
+// 32-column blocks [(w&1)*RB, +RB).
 // With WG (the write-gated variant) each token's phi(K) row is first scaled by
 // its write strength sigma(W_n), W one logit per token and head ([B,H,N]); the
 // scaled row, rounded to bf16, feeds both the MFMA and the normaliser sum.
-// TIn: uint16_t for bf16 inputs, uint8_t for fp8; an fp8 tile holds 128 tokens
-// so that a tile is the same number of bytes (and 16-byte loads) either way.
+// TIn: uint16_t for bf16 inputs, uint8_t for fp8 (16 features per load, so two
+// 8 x 8 blocks per load row).
+
+// Physical 16-byte chunk of logical chunk c in feature row `row` of a tile with
+// CH chunks per row: c ^ t_swz<CH>(row). The 16 lanes of one operand read take
+// 16 consecutive rows (one bank group each); the 16 lanes of one block write take
+// rows 8 or 16 apart, spread at most two to a bank group.
+template <int CH>
+__device__ __forceinline__ int t_swz(int row) {
+  if constexpr (CH >= 16) return (row ^ (row >> 3)) & 15;
+  else return ((row >> 1) ^ (row >> 3)) & 7;
+}
+
+// 8 x 8 transpose of bf16: in[i] holds 8 features of token i, out[h] the 8
+// tokens of feature h (v_perm_b32 takes bytes 0-3 from its second operand and
+// 4-7 from its first).
+__device__ __forceinline__ void transpose8x8(const u32x4* in, u32x4* out) {
+#pragma unroll
+  for (int h = 0; h < 8; ++h) {
+    const uint32_t sel = (h & 1) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      out[h][d] = __builtin_amdgcn_perm(in[2 * d + 1][h >> 1], in[2 * d][h >> 1], sel);
+  }
+}
+
 template <int D, bool WG, typename TIn>
 __global__ __launch_bounds__(256) void linear_state_bf16(const TIn* __restrict__ K,
                                                          const TIn* __restrict__ V,
@@ -81,27 +111,30 @@ __global__ __launch_bounds__(256) void linear_state_bf16(const TIn* __restrict__
                                                          float* __restrict__ part, int N, int T,
                                                          int C) {
   constexpr bool F8 = sizeof(TIn) == 1;
-  constexpr int EPL = 16 / sizeof(TIn);    // elements per 16-byte load
-  constexpr int HALVES = EPL / 8;          // bf16 operands per load
-  constexpr int CH = D / EPL;              // loads per token row
-  constexpr int TILE = 64 * HALVES;        // tokens per LDS tile
-  constexpr int LOADS = TILE * CH / 256;   // loads per thread per tensor per tile
-  constexpr int RS = D + 8;                // LDS row stride in elements (pads banks)
+  constexpr int EPL = 16 / sizeof(TIn);    // features per 16-byte load
+  constexpr int HALVES = EPL / 8;          // 8 x 8 blocks per load row
+  constexpr int FC = D / EPL;              // feature chunks per token row
+  constexpr int TILE = 1024 * EPL / D;     // tokens per tile: 128 blocks per tensor
+  constexpr int TG = TILE / 8;             // 8-token groups per tile
+  constexpr int CH = TILE / 8;             // 16-byte chunks per feature row
   constexpr int RB = D / 64;               // 32-wide blocks per wave per side
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[TILE * RS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[TILE * RS];
+  static_assert(TG * FC == 128, "one block per thread and tensor");
+  __shared__ __attribute__((aligned(16))) uint16_t Kt[D * TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = blockIdx.x, bh = blockIdx.y;
   const int n0 = c * T;
   const int n1 = min(N, n0 + T);
   const size_t base = (size_t)bh * N * D;
-  const TIn* Kh = K + base;
-  const TIn* Vh = V + base;
-
-  u32x4 kr[LOADS], vr[LOADS];  // raw bytes as loaded
-  TIn wr[LOADS];
+  const bool isk = tid < 128;  // waves 0-1: K blocks, waves 2-3: V blocks
+  const int jb = tid & 127, fc = jb % FC, tg = jb / FC;
+  const TIn* src = (isk ? K : V) + base + fc * EPL;
+  uint16_t* tile = isk ? Kt : Vt;
   const TIn* Wh = WG ? W + (size_t)bh * N : nullptr;
+
+  u32x4 raw[8];  // rows 8tg .. 8tg+7 of the tile, raw bytes as loaded
+  TIn wr[8];
   float zacc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) zacc[e] = 0.f;
@@ -113,68 +146,70 @@ __global__ __launch_bounds__(256) void linear_state_bf16(const TIn* __restrict__
 
   auto load_tile = [&](int t0) {
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int chunk = tid + 256 * i;
-      const int n = t0 + chunk / CH, col = (chunk % CH) * EPL;
+    for (int i = 0; i < 8; ++i) {
+      const int n = t0 + 8 * tg + i;
       if (n < n1) {
-        kr[i] = ldg16_stream(Kh + (size_t)n * D + col);
-        vr[i] = ldg16_stream(Vh + (size_t)n * D + col);
-        if (WG) wr[i] = Wh[n];
+        raw[i] = ldg16_stream(src + (size_t)n * D);
+        if (WG) wr[i] = isk ? Wh[n] : TIn(0);
       } else {
-        kr[i] = (u32x4){0, 0, 0, 0};
-        vr[i] = (u32x4){0, 0, 0, 0};
+        raw[i] = (u32x4){0, 0, 0, 0};
         if (WG) wr[i] = 0;
       }
     }
   };
 
-  const int r = lane & 31, h = lane >> 5;
+  const int r = lane & 31, h2 = lane >> 5;
   const int ib0 = (wave >> 1) * RB, jb0 = (wave & 1) * RB;
   const int ntiles = (n1 - n0 + TILE - 1) / TILE;
 
   load_tile(n0);
   for (int it = 0; it < ntiles; ++it) {
     __syncthreads();  // every wave is done reading the previous tile
+    float beta[8];
+    if (WG && isk) {
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int chunk = tid + 256 * i;
-      const int row = chunk / CH, col = (chunk % CH) * EPL;
-      float beta = 1.f;
-      if (WG) beta = sigmoid(elem_f32(wr[i]));
+      for (int i = 0; i < 8; ++i) beta[i] = sigmoid(elem_f32(wr[i]));
+    }
 #pragma unroll
-      for (int hh = 0; hh < HALVES; ++hh) {
-        u32x4 kk = relu_bf16x8(F8 ? fp8_half(kr[i], hh) : kr[i]);
-        const u32x4 vv = F8 ? fp8_half(vr[i], hh) : vr[i];
-        if (WG) {
+    for (int hh = 0; hh < HALVES; ++hh) {
+      u32x4 rows[8], cols[8];
 #pragma unroll
-          for (int p = 0; p < 4; ++p) kk[p] = pack_bf16(bf_lo(kk[p]) * beta, bf_hi(kk[p]) * beta);
+      for (int i = 0; i < 8; ++i) rows[i] = F8 ? fp8_half(raw[i], hh) : raw[i];
+      if (isk) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          rows[i] = relu_bf16x8(rows[i]);
+          if (WG) {
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+              rows[i][p] = pack_bf16(bf_lo(rows[i][p]) * beta[i], bf_hi(rows[i][p]) * beta[i]);
+          }
         }
+      }
+      transpose8x8(rows, cols);
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          zacc[8 * hh + 2 * p] += bf_lo(kk[p]);
-          zacc[8 * hh + 2 * p + 1] += bf_hi(kk[p]);
+      for (int h = 0; h < 8; ++h) {
+        const int row = fc * EPL + 8 * hh + h;
+        *reinterpret_cast<u32x4*>(&tile[row * TILE + ((tg ^ t_swz<CH>(row)) * 8)]) = cols[h];
+        if (isk) {
+          // the normaliser sums the same rounded values the MFMA consumes
+#pragma unroll
+          for (int d = 0; d < 4; ++d) zacc[8 * hh + h] = add_bf16x2(cols[h][d], zacc[8 * hh + h]);
         }
-        *reinterpret_cast<u32x4*>(&Ks[row * RS + col + 8 * hh]) = kk;
-        *reinterpret_cast<u32x4*>(&Vs[row * RS + col + 8 * hh]) = vv;
       }
     }
     __syncthreads();
     if (it + 1 < ntiles) load_tile(n0 + (it + 1) * TILE);  // in flight during the MFMAs
 #pragma unroll
     for (int s = 0; s < TILE / 16; ++s) {
-      const int tok = 16 * s + 8 * h;
+      const int lc = 2 * s + h2;  // logical chunk: tokens 16s + 8h2 .. +7
       u32x4 a[RB], b[RB];
 #pragma unroll
       for (int x = 0; x < RB; ++x) {
         const int fi = (ib0 + x) * 32 + r;
         const int fj = (jb0 + x) * 32 + r;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          a[x][p] = uint32_t(Ks[(tok + 2 * p) * RS + fi]) |
-                    (uint32_t(Ks[(tok + 2 * p + 1) * RS + fi]) << 16);
-          b[x][p] = uint32_t(Vs[(tok + 2 * p) * RS + fj]) |
-                    (uint32_t(Vs[(tok + 2 * p + 1) * RS + fj]) << 16);
-        }
+        a[x] = *reinterpret_cast<const u32x4*>(&Kt[fi * TILE + ((lc ^ t_swz<CH>(fi)) * 8)]);
+        b[x] = *reinterpret_cast<const u32x4*>(&Vt[fj * TILE + ((lc ^ t_swz<CH>(fj)) * 8)]);
       }
 #pragma unroll
       for (int x = 0; x < RB; ++x)
@@ -185,7 +220,7 @@ __global__ __launch_bounds__(256) void linear_state_bf16(const TIn* __restrict__
 
   // partial S, stored in the output pass's fragment order (fp32, see frag_pos)
   // so the reduce reads and writes whole fragments contiguously. C-tile element
-  // (q*4 + e) of lane (col r, half h) is row q*8 + 4h + e: 4 consecutive slots.
+  // (q*4 + e) of lane (col r, half h2) is row q*8 + 4h2 + e: 4 consecutive slots.
   float* P = part + ((size_t)bh * C + c) * (size_t)(D * D + D);
 #pragma unroll
   for (int x = 0; x < RB; ++x)
@@ -193,22 +228,23 @@ __global__ __launch_bounds__(256) void linear_state_bf16(const TIn* __restrict__
     for (int y = 0; y < RB; ++y)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int row = (ib0 + x) * 32 + 8 * q + 4 * h, col = (jb0 + y) * 32 + r;
+        const int row = (ib0 + x) * 32 + 8 * q + 4 * h2, col = (jb0 + y) * 32 + r;
         *reinterpret_cast<f32x4*>(&P[frag_pos<D, F8>(row, col)]) =
             (f32x4){acc[x][y][q * 4], acc[x][y][q * 4 + 1], acc[x][y][q * 4 + 2], acc[x][y][q * 4 + 3]};
       }
 
-  // partial z: thread tid always loaded feature chunk (tid % CH); sum the
-  // 256/CH threads of each chunk in a fixed order
+  // partial z: the K thread of block (fc, tg) holds features fc*EPL .. +EPL over
+  // its token groups; sum the TG groups of each feature in a fixed order
   __syncthreads();
-  float* zred = reinterpret_cast<float*>(Ks);  // 256 * EPL floats fit in the K tile
+  float* zred = reinterpret_cast<float*>(Kt);  // TG * D floats fit in the K tile
+  if (isk) {
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) zred[tid * EPL + e] = zacc[e];
+    for (int e = 0; e < EPL; ++e) zred[tg * D + fc * EPL + e] = zacc[e];
+  }
   __syncthreads();
   if (tid < D) {
-    const int cc = tid / EPL, e = tid % EPL;
     float sum = 0.f;
-    for (int m = 0; m < 256 / CH; ++m) sum += zred[(cc + CH * m) * EPL + e];
+    for (int g = 0; g < TG; ++g) sum += zred[g * D + tid];
     P[D * D + tid] = sum;
   }
 }

@@ -86,8 +86,9 @@ int hla_abi_version(void);
 const char* hla_status_str(int status);
 
 /* Bytes of device workspace hla_linear_fwd (and the stack call) needs for `d`:
- * per-chunk partial states B*H*C*(D*D + D) fp32 plus the reduced state in the
- * form the output pass reads. Host-only and pure: equal dims give equal sizes.
+ * per-chunk partial states, B*H*C of them (D*D + D fp32 on the fp32 path; D*D
+ * bf16 + D fp32 on the bf16 and fp8 paths), plus the reduced state in the form
+ * the output pass reads. Host-only and pure: equal dims give equal sizes.
  * Returns 0 for invalid or unsupported dims, and for empty tensors. */
 size_t hla_linear_workspace_bytes(const hla_dims* d);
 

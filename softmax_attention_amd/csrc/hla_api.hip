@@ -92,7 +92,10 @@ LinearPlan linear_plan(const hla_dims& d) {
   const int64_t max_p = (N + 63) / 64;
   P = P < 1 ? 1 : (P > max_p ? max_p : P);
   p.P = int(P);
-  const size_t part = size_t(BH) * size_t(c) * size_t(D * D + D) * 4;
+  // per chunk: fp32 S and z (fp32 path), or bf16 S and fp32 z (bf16 and fp8 paths)
+  const size_t per_chunk = d.in_dtype != HLA_F32 ? size_t(D * D) * 2 + size_t(D) * 4
+                                                 : size_t(D * D + D) * 4;
+  const size_t part = size_t(BH) * size_t(c) * per_chunk;
   if (d.in_dtype != HLA_F32)
     p.state_bytes = size_t((D / 16 + 1) * (D / 32)) * 1024;  // MFMA operand fragments
   else

@@ -3,9 +3,10 @@
 // Three launches per call:
 //   1. state pass   per (token chunk, b, h): S_c = phi(K_c)^T V_c and
 //                   z_c = sum phi(K_c), with the contraction over tokens on
-//                   32x32x16 bf16 MFMA (fp32 accumulate); partials to workspace.
-//   2. reduce       per (b, h): S = sum_c S_c and z = sum_c z_c in a fixed chunk
-//                   order (deterministic, no float atomics), written straight into
+//                   32x32x16 bf16 MFMA (fp32 accumulate); partials to workspace
+//                   (S_c rounded to bf16, z_c in fp32).
+//   2. reduce       per (b, h): S = sum_c S_c and z = sum_c z_c in fp32 in a fixed
+//                   chunk order (deterministic, no float atomics), written straight into
 //                   the operand fragments the output pass feeds to the MFMA:
 //                   S^T rounded to bf16, z split into a bf16 hi + lo pair.
 //   3. output pass  per (b, h, token group): O = sigma(G) (.) (phi(Q) S) /
@@ -62,6 +63,16 @@ __device__ __forceinline__ int z_run(int t, int kg) {
   return F8 ? 64 * (t >> 1) + 16 * kg + 8 * (t & 1) : 32 * t + 8 * kg;
 }
 
+// One chunk's partial state in the workspace: D*D bf16 of S in frag_pos order,
+// then D fp32 of z. S is rounded to bf16 once more before the fp32 sum of the
+// chunks (the sum is rounded to bf16 for the output pass anyway), which halves
+// the partials' traffic; z, which sets every output's normaliser, stays fp32.
+template <int D>
+struct Partial {
+  static constexpr size_t kSBytes = size_t(D) * D * 2;
+  static constexpr size_t kBytes = kSBytes + size_t(D) * 4;
+};
+
 // ---------------------------------------------------------------------------
 // 1. state pass
 // ---------------------------------------------------------------------------
@@ -108,7 +119,7 @@ template <int D, bool WG, typename TIn>
 __global__ __launch_bounds__(256) void linear_state_bf16(const TIn* __restrict__ K,
                                                          const TIn* __restrict__ V,
                                                          const TIn* __restrict__ W,
-                                                         float* __restrict__ part, int N, int T,
+                                                         char* __restrict__ part, int N, int T,
                                                          int C) {
   constexpr bool F8 = sizeof(TIn) == 1;
   constexpr int EPL = 16 / sizeof(TIn);    // features per 16-byte load
@@ -218,10 +229,12 @@ __global__ __launch_bounds__(256) void linear_state_bf16(const TIn* __restrict__
     }
   }
 
-  // partial S, stored in the output pass's fragment order (fp32, see frag_pos)
+  // partial S, stored in the output pass's fragment order (bf16, see frag_pos)
   // so the reduce reads and writes whole fragments contiguously. C-tile element
   // (q*4 + e) of lane (col r, half h2) is row q*8 + 4h2 + e: 4 consecutive slots.
-  float* P = part + ((size_t)bh * C + c) * (size_t)(D * D + D);
+  char* Pc = part + ((size_t)bh * C + c) * Partial<D>::kBytes;
+  uint16_t* PS = reinterpret_cast<uint16_t*>(Pc);
+  float* Pz = reinterpret_cast<float*>(Pc + Partial<D>::kSBytes);
 #pragma unroll
   for (int x = 0; x < RB; ++x)
 #pragma unroll
@@ -229,8 +242,9 @@ __global__ __launch_bounds__(256) void linear_state_bf16(const TIn* __restrict__
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int row = (ib0 + x) * 32 + 8 * q + 4 * h2, col = (jb0 + y) * 32 + r;
-        *reinterpret_cast<f32x4*>(&P[frag_pos<D, F8>(row, col)]) =
-            (f32x4){acc[x][y][q * 4], acc[x][y][q * 4 + 1], acc[x][y][q * 4 + 2], acc[x][y][q * 4 + 3]};
+        *reinterpret_cast<u32x2*>(&PS[frag_pos<D, F8>(row, col)]) =
+            (u32x2){pack_bf16(acc[x][y][q * 4], acc[x][y][q * 4 + 1]),
+                    pack_bf16(acc[x][y][q * 4 + 2], acc[x][y][q * 4 + 3])};
       }
 
   // partial z: the K thread of block (fc, tg) holds features fc*EPL .. +EPL over
@@ -245,7 +259,7 @@ __global__ __launch_bounds__(256) void linear_state_bf16(const TIn* __restrict__
   if (tid < D) {
     float sum = 0.f;
     for (int g = 0; g < TG; ++g) sum += zred[g * D + tid];
-    P[D * D + tid] = sum;
+    Pz[tid] = sum;
   }
 }
 
@@ -254,36 +268,46 @@ __global__ __launch_bounds__(256) void linear_state_bf16(const TIn* __restrict__
 // ---------------------------------------------------------------------------
 // The state pass already stored its partials in the numerator fragments' order
 // (frag_pos). Fragment (NJ, t) of the denominator holds z_hi[row(t, k)] in rows
-// 0..7 and z_lo[row(t, k)] in rows 8..15. Chunks are summed in order
+// 0..7 and z_lo[row(t, k)] in rows 8..15. Chunks are summed in fp32 in order
 // c = 0, 1, ..., C-1 (four independent loads in flight per step).
 template <int D, bool F8>
-__global__ __launch_bounds__(256) void linear_reduce_bf16(const float* __restrict__ part,
+__global__ __launch_bounds__(256) void linear_reduce_bf16(const char* __restrict__ part,
                                                           uint32_t* __restrict__ state, int C) {
   constexpr int NT = D / 32, NJ = D / 16, NF = (NJ + 1) * NT;
   constexpr int NUM_WG = D * D / 8 / 256;  // workgroups for the numerator fragments
+  constexpr size_t kStride = Partial<D>::kBytes;
   const int bh = blockIdx.y, tid = threadIdx.x;
-  const size_t stride = (size_t)D * D + D;
-  const float* P = part + (size_t)bh * C * stride;
+  const char* P = part + (size_t)bh * C * kStride;
   uint32_t* St = state + (size_t)bh * NF * 256;
-  auto sum8 = [&](size_t off, float* v) {
-    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+  // 8 consecutive S slots (16 bytes of bf16) at slot `off`, summed over the chunks
+  auto sum8_s = [&](size_t off, float* v) {
+    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     int c = 0;
+    auto add = [&](const u32x4 w) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        a[2 * q] += bf_lo(w[q]);
+        a[2 * q + 1] += bf_hi(w[q]);
+      }
+    };
     for (; c + 4 <= C; c += 4) {
-      f32x4 x[8];
+      u32x4 x[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        x[2 * u] = *reinterpret_cast<const f32x4*>(P + (c + u) * stride + off);
-        x[2 * u + 1] = *reinterpret_cast<const f32x4*>(P + (c + u) * stride + off + 4);
-      }
+      for (int u = 0; u < 4; ++u) x[u] = ldg16(P + (c + u) * kStride + off * 2);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        a0 += x[2 * u];
-        a1 += x[2 * u + 1];
-      }
+      for (int u = 0; u < 4; ++u) add(x[u]);
     }
-    for (; c < C; ++c) {
-      a0 += *reinterpret_cast<const f32x4*>(P + c * stride + off);
-      a1 += *reinterpret_cast<const f32x4*>(P + c * stride + off + 4);
+    for (; c < C; ++c) add(ldg16(P + c * kStride + off * 2));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = a[e];
+  };
+  // 8 consecutive z entries (fp32) from entry `off`, summed over the chunks
+  auto sum8_z = [&](size_t off, float* v) {
+    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+    const char* Z = P + Partial<D>::kSBytes + off * 4;
+    for (int c = 0; c < C; ++c) {
+      a0 += *reinterpret_cast<const f32x4*>(Z + c * kStride);
+      a1 += *reinterpret_cast<const f32x4*>(Z + c * kStride + 16);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -294,12 +318,12 @@ __global__ __launch_bounds__(256) void linear_reduce_bf16(const float* __restric
   float v[8];
   if (blockIdx.x < NUM_WG) {
     const int x = blockIdx.x * 256 + tid;  // (fragment, lane) pair; 8 slots each
-    sum8((size_t)x * 8, v);
+    sum8_s((size_t)x * 8, v);
     *reinterpret_cast<u32x4*>(St + (size_t)x * 4) =
         (u32x4){pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]), pack_bf16(v[4], v[5]), pack_bf16(v[6], v[7])};
   } else if (tid < NT * 64) {
     const int t = tid >> 6, l = tid & 63, i = l & 15, g = l >> 4;
-    sum8((size_t)D * D + z_run<D, F8>(t, g), v);
+    sum8_z((size_t)z_run<D, F8>(t, g), v);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float hi = bf16_to_f32(f32_to_bf16(v[e]));
@@ -456,7 +480,7 @@ hipError_t launch_d(const hla_dims& d, const void* q, const void* k, const void*
                     const LinearPlan& plan, hipStream_t stream) {
   const int BH = int(d.B * d.H), N = int(d.N);
   char* wsb = reinterpret_cast<char*>(ws);
-  float* part = reinterpret_cast<float*>(wsb + plan.part_off);
+  char* part = wsb + plan.part_off;
   uint32_t* state = reinterpret_cast<uint32_t*>(wsb + plan.state_off);
   const TIn* Kp = reinterpret_cast<const TIn*>(k);
   const TIn* Vp = reinterpret_cast<const TIn*>(v);

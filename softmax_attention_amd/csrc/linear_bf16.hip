@@ -269,7 +269,7 @@ __global__ __launch_bounds__(256) void linear_state_bf16(const TIn* __restrict__
 // The state pass already stored its partials in the numerator fragments' order
 // (frag_pos). Fragment (NJ, t) of the denominator holds z_hi[row(t, k)] in rows
 // 0..7 and z_lo[row(t, k)] in rows 8..15. Chunks are summed in fp32 in order
-// c = 0, 1, ..., C-1 (four independent loads in flight per step).
+// c = 0, 1, ..., C-1, with the loads of eight chunks in flight at a time.
 template <int D, bool F8>
 __global__ __launch_bounds__(256) void linear_reduce_bf16(const char* __restrict__ part,
                                                           uint32_t* __restrict__ state, int C) {
@@ -290,12 +290,12 @@ __global__ __launch_bounds__(256) void linear_reduce_bf16(const char* __restrict
         a[2 * q + 1] += bf_hi(w[q]);
       }
     };
-    for (; c + 4 <= C; c += 4) {
-      u32x4 x[4];
+    for (; c + 8 <= C; c += 8) {
+      u32x4 x[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) x[u] = ldg16(P + (c + u) * kStride + off * 2);
+      for (int u = 0; u < 8; ++u) x[u] = ldg16(P + (c + u) * kStride + off * 2);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) add(x[u]);
+      for (int u = 0; u < 8; ++u) add(x[u]);
     }
     for (; c < C; ++c) add(ldg16(P + c * kStride + off * 2));
 #pragma unroll
@@ -305,7 +305,21 @@ __global__ __launch_bounds__(256) void linear_reduce_bf16(const char* __restrict
   auto sum8_z = [&](size_t off, float* v) {
     f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
     const char* Z = P + Partial<D>::kSBytes + off * 4;
-    for (int c = 0; c < C; ++c) {
+    int c = 0;
+    for (; c + 8 <= C; c += 8) {
+      f32x4 x[16];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        x[2 * u] = *reinterpret_cast<const f32x4*>(Z + (c + u) * kStride);
+        x[2 * u + 1] = *reinterpret_cast<const f32x4*>(Z + (c + u) * kStride + 16);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        a0 += x[2 * u];
+        a1 += x[2 * u + 1];
+      }
+    }
+    for (; c < C; ++c) {
       a0 += *reinterpret_cast<const f32x4*>(Z + c * kStride);
       a1 += *reinterpret_cast<const f32x4*>(Z + c * kStride + 16);
     }

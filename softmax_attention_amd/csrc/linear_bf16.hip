@@ -385,27 +385,26 @@ __global__ __launch_bounds__(256, 2) void linear_out_bf16(const TIn* __restrict_
   int grp = blockIdx.x * 4 + wave;
   if (grp * 16 >= N) return;
 
-  u32x4 qv[NU], gv[NU];  // raw bytes as loaded
+  // Buffer loads over the head: a token past N reads zeros without touching
+  // memory, so every prefetch is issued unconditionally and the compiler can
+  // wait for exactly the oldest group instead of draining every load. (Offsets
+  // of prefetches beyond the last group may wrap 32 bits; they stay inside the
+  // head, and their values are never used.)
+  const uint32_t head_bytes = (uint32_t)((size_t)N * D * sizeof(TIn));
+  const rsrc_t Qr = make_rsrc(Qh, head_bytes), Gr = make_rsrc(Gh, head_bytes);
   auto load = [&](int gi, u32x4* qd, u32x4* gd) {
-    const int tok = gi * 16 + n;
+    const uint32_t off = ((uint32_t)(gi * 16 + n) * D + EPL * g) * sizeof(TIn);
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-      if (tok < N) {
-        qd[u] = ldg16(Qh + (size_t)tok * D + 4 * EPL * u + EPL * g);
-        gd[u] = ldg16(Gh + (size_t)tok * D + 4 * EPL * u + EPL * g);
-      } else {
-        qd[u] = (u32x4){0, 0, 0, 0};
-        gd[u] = (u32x4){0, 0, 0, 0};
-      }
+      qd[u] = buf_load16(Qr, off + 4 * EPL * u * sizeof(TIn));
+      gd[u] = buf_load16(Gr, off + 4 * EPL * u * sizeof(TIn));
     }
   };
-  load(grp, qv, gv);
-
-  for (; grp * 16 < N; grp += stride) {
-    u32x4 qn[NU], gn[NU];
-    const bool more = (grp + stride) * 16 < N;
-    if (more) load(grp + stride, qn, gn);
-
+  // Two groups ahead in flight, in three register sets used in turn (the loop
+  // is unrolled by three, so no set is copied into another: a copy would have
+  // to wait for the loads it reads).
+  u32x4 qa[NU], ga[NU], qb[NU], gb[NU], qc[NU], gc[NU];
+  auto compute = [&](int gi, const u32x4* qv, const u32x4* gv) __attribute__((always_inline)) {
     // Re-read the fragments from LDS every group: an opaque (always zero)
     // offset keeps the compiler from hoisting all of them into registers,
     // which would cost the occupancy this streaming loop needs.
@@ -424,7 +423,7 @@ __global__ __launch_bounds__(256, 2) void linear_out_bf16(const TIn* __restrict_
     const float den = add_halves(accd[0]) + eps;
     const float rden = 1.0f / den;
 
-    const int tok = grp * 16 + n;
+    const int tok = gi * 16 + n;
     if (tok < N) {
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
@@ -478,13 +477,19 @@ __global__ __launch_bounds__(256, 2) void linear_out_bf16(const TIn* __restrict_
         }
       }
     }
-    if (more) {
-#pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        qv[u] = qn[u];
-        gv[u] = gn[u];
-      }
-    }
+};
+  load(grp, qa, ga);
+  load(grp + stride, qb, gb);
+  for (;;) {
+    load(grp + 2 * stride, qc, gc);
+    compute(grp, qa, ga);
+    if ((grp += stride) * 16 >= N) break;
+    load(grp + 2 * stride, qa, ga);
+    compute(grp, qb, gb);
+    if ((grp += stride) * 16 >= N) break;
+    load(grp + 2 * stride, qb, gb);
+    compute(grp, qc, gc);
+    if ((grp += stride) * 16 >= N) break;
   }
 }
 

@@ -371,19 +371,12 @@ __global__ __launch_bounds__(256, 2) void linear_out_bf16(const TIn* __restrict_
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bh = blockIdx.y;
-  {
-    const u32x4* src = reinterpret_cast<const u32x4*>(state + (size_t)bh * NF * 256);
-    for (int x = tid; x < NF * 64; x += 256) fr[x] = src[x];
-  }
-  __syncthreads();
-
   const int n = lane & 15, g = lane >> 4;
   const size_t base = (size_t)bh * N * D;
   const TIn* Qh = Q + base;
   const TIn* Gh = G + base;
   const int stride = gridDim.x * 4;
   int grp = blockIdx.x * 4 + wave;
-  if (grp * 16 >= N) return;
 
   // Buffer loads over the head: a token past N reads zeros without touching
   // memory, so every prefetch is issued unconditionally and the compiler can
@@ -400,10 +393,28 @@ __global__ __launch_bounds__(256, 2) void linear_out_bf16(const TIn* __restrict_
       gd[u] = buf_load16(Gr, off + 4 * EPL * u * sizeof(TIn));
     }
   };
+
+  // The head's state fragments go to LDS; the first two groups' Q and G loads
+  // are issued after the fragment loads and before the wait for them, so the
+  // two latencies overlap (loads complete in order: waiting for the fragments
+  // leaves the newer Q/G loads in flight).
+  constexpr int FPT = (NF * 64 + 255) / 256;  // fragment loads per thread
+  const rsrc_t Sr = make_rsrc(state + (size_t)bh * NF * 256, NF * 64 * 16);
+  u32x4 frv[FPT];
+#pragma unroll
+  for (int i = 0; i < FPT; ++i) frv[i] = buf_load16(Sr, (tid + 256 * i) * 16);
   // Two groups ahead in flight, in three register sets used in turn (the loop
   // is unrolled by three, so no set is copied into another: a copy would have
   // to wait for the loads it reads).
   u32x4 qa[NU], ga[NU], qb[NU], gb[NU], qc[NU], gc[NU];
+  load(grp, qa, ga);
+  load(grp + stride, qb, gb);
+#pragma unroll
+  for (int i = 0; i < FPT; ++i)
+    if (tid + 256 * i < NF * 64) fr[tid + 256 * i] = frv[i];
+  __syncthreads();
+  if (grp * 16 >= N) return;
+
   auto compute = [&](int gi, const u32x4* qv, const u32x4* gv) __attribute__((always_inline)) {
     // Re-read the fragments from LDS every group: an opaque (always zero)
     // offset keeps the compiler from hoisting all of them into registers,
@@ -477,9 +488,7 @@ __global__ __launch_bounds__(256, 2) void linear_out_bf16(const TIn* __restrict_
         }
       }
     }
-};
-  load(grp, qa, ga);
-  load(grp + stride, qb, gb);
+  };
   for (;;) {
     load(grp + 2 * stride, qc, gc);
     compute(grp, qa, ga);

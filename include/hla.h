@@ -121,7 +121,7 @@ hla_status hla_linear_write_gated_fwd(const hla_dims* d, const void* q, const vo
 /* Bytes of device workspace hla_softmax_anchor_fwd needs for `d`: on the bf16
  * and fp8 paths a repacked copy of V (B*H*D*ceil(N/64)*64 bf16, V transposed with zero
  * keys past N) followed by room for the partial results of up to
- * P = min(256, ceil(N/256) * B*H * ceil(N/64)) key-range pieces (P*256*(D+2)
+ * P = min(1024, ceil(N/256) * B*H * ceil(N/64)) key-range pieces (P*256*(D+2)
  * fp32), used when the query blocks of an incomplete last batch of workgroups
  * are split along the keys; 0 on the fp32 path. Host-only and pure; 0 for
  * invalid or unsupported dims and for empty tensors. */

@@ -42,7 +42,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kBR = 32 * kWaves;        // query rows per workgroup
 constexpr int kBC = 64;   // keys per LDS tile
 constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
-constexpr int kMaxPieces = 256;  // most key-range pieces one call splits its last batch into
+constexpr int kMaxPieces = 1024;  // most key-range pieces one call splits its last batch into
 
 // LDS tiles use XOR swizzles of whole 16-byte chunks instead of padding. A
 // 16-byte LDS read serves 16 lanes per cycle from the 64 banks (16 bank groups
@@ -638,11 +638,29 @@ hipError_t launch_d(const hla_dims& d, const void* q, const void* k, const void*
   // incomplete last batch are split along the keys so that batch takes a
   // fraction of a full one.
   const int slots = device_cus();
+  // Split each of the `tail` blocks into k pieces. The last batch then lasts
+  // ceil(tail k / slots) / k rounds; take the smallest k within 0.02 rounds of
+  // the shortest (more pieces cost partial results and combine work), within
+  // the piece cap and at least one key tile per piece.
   int tail = total % slots, split = 1;
   if (tail > 0) {
-    split = slots / tail;
-    if (split > ntiles) split = ntiles;
-    if (split > L.pieces_cap / tail) split = L.pieces_cap / tail;
+    const int kmax_t = ntiles, kmax_p = L.pieces_cap / tail;
+    const int kmax = kmax_t < kmax_p ? kmax_t : kmax_p;
+    int best_num = 1, best_den = 1;  // shortest length in rounds, as a fraction
+    for (int k = 2; k <= kmax; ++k) {
+      const int num = (tail * k + slots - 1) / slots;
+      if (num * best_den < best_num * k) {
+        best_num = num;
+        best_den = k;
+      }
+    }
+    for (int k = 2; k <= kmax; ++k) {
+      const int num = (tail * k + slots - 1) / slots;
+      if (50 * num * best_den <= (50 * best_num + best_den) * k) {  // num/k <= best + 1/50
+        split = k;
+        break;
+      }
+    }
   }
   if (split < 2) {
     tail = 0;

@@ -188,14 +188,14 @@ def test_softmax_argument_errors():
 
 def test_softmax_workspace_size():
     # repacked V^T (B*H*D*ceil(N/64)*64 bf16), then room for the partial results
-    # of up to P = min(256, query blocks * key tiles) key-range pieces of 256
+    # of up to P = min(1024, query blocks * key tiles) key-range pieces of 256
     # query rows: D fp32 values plus (max, sum) each; every part rounded up to
     # 256 bytes
     up = lambda x: -(-x // 256) * 256
     for (B, H, N, D) in [(2, 16, 19320, 128), (1, 2, 1, 64), (1, 1, 64, 128), (1, 1, 65, 128),
                          (1, 2, 1000, 128)]:
         n_pad = -(-N // 64) * 64
-        pieces = min(256, B * H * -(-N // 256) * (n_pad // 64))
+        pieces = min(1024, B * H * -(-N // 256) * (n_pad // 64))
         want = up(B * H * D * n_pad * 2) + up(pieces * 256 * D * 4) + up(pieces * 256 * 2 * 4)
         assert hla.hla_softmax_anchor_workspace_bytes(dims(B, H, N, D)) == want
     assert hla.hla_softmax_anchor_workspace_bytes(dims(N=0)) == 0

@@ -281,6 +281,25 @@ def test_softmax_split_last_round_full():
     assert rel_err(acc.cpu() - base, ref) <= TOL[torch.bfloat16]
 
 
+def test_softmax_large_tail_split_sampled():
+    # 720p x 81 frames with B = 1: 1216 query blocks leave a last batch of 192 on
+    # 256 CUs, which is split four ways (768 pieces, three quarter-length
+    # batches); sampled rows against the oracle, plain and accumulating
+    from hla_inputs import duration_workload
+    w = duration_workload(81, B=1, H=16)
+    q, k, v, g = layer_inputs(w, 0)
+    rows = sample_rows(w.N, count=24, seed=810)
+    ref = oracle.gated_softmax(q, k, v, g, w.scale, rows=rows)
+    sm = run_softmax(q, k, v, g, w.scale)
+    e = rel_err(sm[..., rows, :], ref)
+    base = custom((w.B, w.H, w.N, w.D), 8100, torch.float32, n=1)[0]
+    acc = base.to(DEV)
+    run_softmax(q, k, v, g, w.scale, accumulate=True, out=acc)
+    e_acc = rel_err((acc.cpu() - base)[..., rows, :], ref)
+    print(f"[{w.name} B=1] softmax err {e:.3e}, accumulated {e_acc:.3e}", flush=True)
+    assert e <= TOL[torch.bfloat16] and e_acc <= TOL[torch.bfloat16]
+
+
 def test_duration_sweep_longest_sampled():
     # 720p x 961 frames (60 s at 16 fps): N = 221,720 tokens, two heads; the
     # linear layer in full, the softmax anchor on sampled query rows

@@ -603,3 +603,33 @@ def test_linear_beyond_2gib_per_tensor():
     e = rel_err(out[..., rows, :], ref)
     print(f"[max-size linear] err {e:.3e} on {len(rows)} rows", flush=True)
     assert e <= TOL[torch.bfloat16]
+
+
+def test_concurrent_calls_on_two_streams():
+    # calls on different streams with their own workspaces may run at the same
+    # time: each must give exactly its sequential result
+    B, H, N, D = 1, 4, 3000, 128
+    q, k, v, g = (t.to(DEV) for t in make((B, H, N, D), 9400, torch.bfloat16))
+    q2, k2, v2, g2 = (t.to(DEV) for t in make((B, H, N, D), 9500, torch.bfloat16))
+    ref_l = hla.hla_linear_fwd(q, k, v, g)
+    ref_a = hla.hla_softmax_anchor_fwd(q2, k2, v2, g2)
+    ref_l2 = hla.hla_linear_fwd(q2, k2, v2, g2)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for rep in range(3):
+        out_l, out_a, out_l2 = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        ws1, ws2 = hla.linear_workspace(q), hla.anchor_workspace(q)
+        ws3 = hla.linear_workspace(q)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s1):
+            hla.hla_softmax_anchor_fwd(q2, k2, v2, g2, out=out_a, workspace=ws2)
+        with torch.cuda.stream(s2):
+            hla.hla_linear_fwd(q, k, v, g, out=out_l, workspace=ws1)
+            hla.hla_linear_fwd(q2, k2, v2, g2, out=out_l2, workspace=ws3)
+        torch.cuda.synchronize()
+        outs.append((out_l, out_a, out_l2))
+    for out_l, out_a, out_l2 in outs:
+        assert torch.equal(out_l, ref_l)
+        assert torch.equal(out_a, ref_a)
+        assert torch.equal(out_l2, ref_l2)

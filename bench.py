@@ -139,7 +139,8 @@ def cpu_baseline(w, budget_s: float):
         "value": w.B * w.N / step_s, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
         "sample": (f"fp64 numpy oracle: gated linear on 1 of {heads} heads at N={w.N} and gated "
                    f"softmax on {len(rows)} query rows of that head, {n_lin} reps in "
-                   f"{t_lin + t_sm:.1f} s, scaled to B*H={heads} heads and all N rows"),
+                   f"{t_lin + t_sm:.1f} s, scaled to B*H={heads} heads and all N rows; "
+                   f"host os.cpu_count()={os.cpu_count()}, BLAS threads={int(cores)}"),
     }
 
 
@@ -229,8 +230,11 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = start.elapsed_time(stop) / K
-    lin_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
-    sm_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    lin_t = sorted(e[0].elapsed_time(e[1]) for e in ev)
+    sm_t = sorted(e[1].elapsed_time(e[2]) for e in ev)
+    lin_ms = sum(lin_t) / K
+    sm_ms = sum(sm_t) / K
+    median = lambda t: (t[(len(t) - 1) // 2] + t[len(t) // 2]) / 2
 
     BH, N, D = w.B * w.H, w.N, w.D
     tokens = w.B * N
@@ -242,12 +246,14 @@ def main():
 
     details = {
         "wall_s_timed": round(wall, 4),
-        "linear": {"ms": round(lin_ms, 4), "tokens_per_s": tokens / (lin_ms * 1e-3),
+        "linear": {"ms": round(lin_ms, 4), "ms_median": round(median(lin_t), 4), "ms_min": round(lin_t[0], 4),
+                   "tokens_per_s": tokens / (lin_ms * 1e-3),
                    "alg_bytes": lin_bytes, "GB_s": round(lin_gbs, 1),
                    "frac_hbm_peak": round(lin_gbs / PEAK_HBM_GBS, 4),
                    "traffic": traffic_for("linear", w.name),
                    "note": "3 launches: state pass, reduce, output pass"},
-        "anchor": {"ms": round(sm_ms, 4), "tokens_per_s": tokens / (sm_ms * 1e-3),
+        "anchor": {"ms": round(sm_ms, 4), "ms_median": round(median(sm_t), 4), "ms_min": round(sm_t[0], 4),
+                   "tokens_per_s": tokens / (sm_ms * 1e-3),
                    "alg_flops": sm_flops, "TFLOP_s": round(sm_tfs, 1),
                    "frac_mfma_peak": round(sm_tfs / PEAK_BF16_TFLOPS, 4)},
         "hybrid_3to1_layer_tokens_per_s": tokens / ((3 * lin_ms + sm_ms) / 4 * 1e-3),
@@ -279,6 +285,7 @@ def main():
         details["attnres_route"] = attnres_timing(torch, hla)
         details["stack"] = stack_timing(torch, hla)
         details["other_workloads"] = [pair_timing(torch, hla, BY_NAME[n]) for n in ("480p_81f", "long_720p_193f")]
+        details["tiny_f32"] = tiny_timing(torch, hla)
 
     line = {
         "metric": METRIC, "value": tokens / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
@@ -384,21 +391,49 @@ def fp8_timing(torch, hla, w, sets, K, lin_ms_bf16, sm_ms_bf16):
     }
 
 
-def pair_timing(torch, hla, w, reps: int = 5):
-    """One gated linear and one gated softmax layer of workload ``w`` (bf16)."""
-    q, k, v, g = gpu_inputs(w, 0, torch)
-    ws_l, ws_a = hla.linear_workspace(q), hla.anchor_workspace(q)
+def tiny_timing(torch, hla, reps: int = 50):
+    """The tiny fp32 pair (B=1, H=2, N=256, D=32): launch-bound, so microseconds only."""
+    from hla_inputs import BY_NAME, layer_inputs
+    w = BY_NAME["tiny_f32"]
+    q, k, v, g = (t.cuda() for t in layer_inputs(w, 0))
     out = torch.empty_like(q)
-    res = {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D}
-    for name, fn in (("linear", lambda: hla.hla_linear_fwd(q, k, v, g, out=out, eps=w.eps, workspace=ws_l)),
-                     ("softmax", lambda: hla.hla_softmax_anchor_fwd(q, k, v, g, out=out, scale=w.scale,
-                                                                    workspace=ws_a))):
+    ws = hla.linear_workspace(q)
+    res = {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D, "dtype": "f32",
+           "note": "launch-bound: time per call, no roofline claim"}
+    for name, fn in (("linear", lambda: hla.hla_linear_fwd(q, k, v, g, out=out, eps=w.eps, workspace=ws)),
+                     ("softmax", lambda: hla.hla_softmax_anchor_fwd(q, k, v, g, out=out, scale=w.scale))):
         fn()
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for _ in range(reps):
             fn()
+        b.record()
+        torch.cuda.synchronize()
+        res[f"{name}_us"] = round(a.elapsed_time(b) / reps * 1e3, 2)
+    return res
+
+
+def pair_timing(torch, hla, w, reps: int = 6):
+    """One gated linear and one gated softmax layer of workload ``w`` (bf16).
+
+    Two input sets alternate, so a call never finds its inputs in the 256 MB
+    Infinity Cache from the previous call.
+    """
+    sets = [gpu_inputs(w, s_, torch) for s_ in range(2)]
+    ws_l, ws_a = hla.linear_workspace(sets[0][0]), hla.anchor_workspace(sets[0][0])
+    out = torch.empty_like(sets[0][0])
+    res = {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D}
+    for name, fn in (("linear", lambda i: hla.hla_linear_fwd(*sets[i % 2], out=out, eps=w.eps, workspace=ws_l)),
+                     ("softmax", lambda i: hla.hla_softmax_anchor_fwd(*sets[i % 2], out=out, scale=w.scale,
+                                                                      workspace=ws_a))):
+        fn(0)
+        fn(1)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(reps):
+            fn(i)
         b.record()
         torch.cuda.synchronize()
         res[f"{name}_ms"] = round(a.elapsed_time(b) / reps, 4)

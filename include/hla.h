@@ -169,9 +169,10 @@ hla_status hla_hybrid_stack_fwd(const hla_dims* d, int n_layers, const int32_t* 
  * HOST array of n_blocks DEVICE pointers, 0 <= n_blocks <= 16 (else HLA_ERR_BAD_ARG);
  * w_router is a DEVICE bf16 [D, D] row-major matrix (q_j = sum_k x_k W[k][j]).
  * q is formed on the matrix cores from x split into a bf16 hi + lo pair (about 16
- * significant bits; fp32 sums); scores, softmax and the mix are fp32. With n_blocks = 0 out = x (a copy, or nothing when
- * out == x). out may be x itself (in place); it must not overlap a summary or W.
- * All device pointers 16-byte aligned. No workspace. */
+ * significant bits; fp32 sums); scores, softmax and the mix are fp32. With
+ * n_blocks = 0 out = x (a copy, or nothing when out == x). out may be x itself
+ * (in place); it must not overlap a summary or W. All device pointers 16-byte
+ * aligned. No workspace. */
 hla_status hla_attnres_route_fwd(const hla_dims* d, int n_blocks, const void* const* summaries,
                                  const void* x, const void* w_router, void* out, void* stream);
 

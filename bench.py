@@ -295,7 +295,7 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": N, "D": D,
                    "latent_thw": list(w.latent),
                    "step": "1 gated linear layer + 1 gated softmax anchor"},
-        "roofline": {"bound": "mfma", "kernel": "anchor_bf16", "achieved": round(sm_tfs, 2),
+        "roofline": {"bound": "mfma", "kernel": "hla_softmax_anchor_fwd (anchor_pack_vt + anchor_bf16 + anchor_combine)", "achieved": round(sm_tfs, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(sm_tfs / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
         "details": details,

@@ -79,6 +79,26 @@ def test_library_exports_every_declared_symbol():
     assert set(declared_functions()) <= exported
 
 
+def test_header_is_plain_c_and_cpp(tmp_path):
+    # every declaration compiles as strict C99 and as C++17, with no HIP or torch header
+    calls = "\n".join(f"  (void)&{fn};" for fn in declared_functions())
+    for lang, std, cc in (("c", "-std=c99", "gcc"), ("c++", "-std=c++17", "g++")):
+        src = tmp_path / f"use.{'c' if lang == 'c' else 'cpp'}"
+        src.write_text(f'#include "hla.h"\nint main(void) {{\n{calls}\n  return HLA_ABI_VERSION == 0;\n}}\n')
+        r = subprocess.run([cc, std, "-Wall", "-Wextra", "-Werror", "-pedantic", "-fsyntax-only",
+                            "-I", os.path.join(ROOT, "include"), str(src)], capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
+
+
+def test_c_client_source_compiles():
+    # the plain C client that a GPU test runs (C99, warnings as errors)
+    src = os.path.join(ROOT, "tests", "c_client", "hla_c_client.c")
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-fsyntax-only",
+                        "-D__HIP_PLATFORM_AMD__", "-isystem", "/opt/rocm/include",
+                        "-I", os.path.join(ROOT, "include"), src], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
 def test_version_and_status_strings():
     assert hla.hla_abi_version() == 4
     for code, name in hla.STATUS.items():

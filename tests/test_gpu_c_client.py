@@ -1,0 +1,72 @@
+"""The library called from a plain C99 program (tests/c_client/hla_c_client.c).
+
+The program allocates device memory and a stream with the HIP runtime itself,
+calls the library through include/hla.h and writes the output's raw bytes; no
+torch or Python runs in its process. Its output must match the fp64 oracle to
+the same tolerance as the binding's, and the binding's own output bit for bit
+(both call the same deterministic kernels on the same bytes).
+"""
+import os
+import subprocess
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import softmax_attention_amd as hla
+from hla_inputs import custom
+
+pytestmark = pytest.mark.gpu
+
+CLIENT = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_client", "hla_c_client")
+FP8 = torch.float8_e4m3fn
+CODE = {torch.float32: 0, torch.bfloat16: 1, FP8: 2}
+RAW = {torch.float32: torch.int32, torch.bfloat16: torch.int16, FP8: torch.uint8}
+
+CASES = [
+    ("linear", (2, 3, 700, 128), torch.bfloat16, torch.bfloat16),
+    ("linear", (1, 2, 257, 32), torch.float32, torch.float32),
+    ("linear", (1, 2, 1000, 64), FP8, torch.float32),
+    ("softmax", (1, 2, 300, 64), torch.bfloat16, torch.float32),
+    ("softmax", (2, 2, 129, 128), FP8, torch.bfloat16),
+    ("softmax", (1, 1, 65, 32), torch.float32, torch.float32),
+]
+
+
+def _to_file(t, path):
+    t.contiguous().view(RAW[t.dtype]).numpy().tofile(path)
+
+
+@pytest.mark.parametrize("op,shape,ind,outd", CASES,
+                         ids=[f"{c[0]}-{'x'.join(map(str, c[1]))}-{str(c[2])[6:]}-{str(c[3])[6:]}"
+                              for c in CASES])
+def test_c_client_matches_oracle_and_binding(tmp_path, op, shape, ind, outd):
+    assert os.path.exists(CLIENT), f"{CLIENT} is missing: run __graft_entry__.build()"
+    print(f"c client {op} {shape} {ind} -> {outd}", flush=True)
+    q, k, v, g = custom(shape, 40000 + sum(shape), ind)
+    for name, t in zip("qkvg", (q, k, v, g)):
+        _to_file(t, tmp_path / f"{name}.bin")
+    B, H, N, D = shape
+    r = subprocess.run([CLIENT, op, str(B), str(H), str(N), str(D), str(CODE[ind]), str(CODE[outd]),
+                        str(tmp_path)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, f"client exited {r.returncode}: {r.stdout} {r.stderr}"
+    assert r.stdout.startswith(f"ok {op} HLA_OK"), r.stdout
+    raw = np.fromfile(tmp_path / "out.bin", dtype=np.uint8)
+    got = torch.from_numpy(raw).view(RAW[outd]).view(outd).reshape(shape)
+
+    if op == "linear":
+        ref = oracle.gated_linear(q, k, v, g, 1e-6)
+    else:
+        ref = oracle.gated_softmax(q, k, v, g, D ** -0.5)
+    tol = 1e-4 if ind == torch.float32 else 2e-2
+    assert oracle.max_rel_error(got.float(), ref) <= tol
+
+    d = [t.to("cuda") for t in (q, k, v, g)]
+    out = torch.empty(shape, dtype=outd, device="cuda")
+    if op == "linear":
+        hla.hla_linear_fwd(*d, out=out, eps=1e-6)
+    else:
+        hla.hla_softmax_anchor_fwd(*d, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu().view(RAW[outd]), got.view(RAW[outd]))

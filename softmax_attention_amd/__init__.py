@@ -130,12 +130,18 @@ def _dtype_code(dt) -> int:
 
 
 def dims_of(q, out_dtype=None) -> hla_dims:
-    """hla_dims of a [B, H, N, D] tensor; out_dtype defaults to q's dtype."""
+    """hla_dims of a [B, H, N, D] tensor.
+
+    out_dtype defaults to the output dtype a call makes when given no output:
+    q's dtype, except bf16 for fp8 inputs (fp8 outputs are not built)."""
     if q.dim() != 4:
         raise ValueError(f"expected [B, H, N, D], got shape {tuple(q.shape)}")
     B, H, N, D = (int(x) for x in q.shape)
     ind = _dtype_code(q)
-    outd = ind if out_dtype is None else _dtype_code(out_dtype)
+    if out_dtype is None:
+        outd = HLA_BF16 if ind == HLA_FP8_E4M3 else ind
+    else:
+        outd = _dtype_code(out_dtype)
     return hla_dims(B, H, N, D, ind, outd)
 
 

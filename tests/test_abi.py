@@ -297,6 +297,10 @@ def test_binding_dims():
     assert hla.dims_of(t.float(), t.float()).in_dtype == F32
     d = hla.dims_of(t.to(torch.float8_e4m3fn), torch.bfloat16)
     assert (d.in_dtype, d.out_dtype) == (FP8, BF16)
+    # fp8 inputs default to bf16 output (as the calls do), so workspace sizes are not 0
+    d = hla.dims_of(t.to(torch.float8_e4m3fn))
+    assert (d.in_dtype, d.out_dtype) == (FP8, BF16)
+    assert hla.hla_linear_workspace_bytes(d) > 0 and hla.hla_softmax_anchor_workspace_bytes(d) > 0
     with pytest.raises(TypeError):
         hla.dims_of(t.half())
 

@@ -36,13 +36,38 @@ __global__ __launch_bounds__(256) void linear_state_f32(const float* __restrict_
 #pragma unroll
     for (int y = 0; y < R; ++y) acc[x][y] = 0.f;
   }
+  // Tile loads are unconditional 16-byte loads (a row past the chunk reads the
+  // chunk's last row and is then zeroed), so they are all in flight at once.
+  constexpr int NV = kTileF * D / 4 / 256;  // 16-byte loads per thread and tensor
+  const f32x4* K4 = reinterpret_cast<const f32x4*>(K + base);
+  const f32x4* V4 = reinterpret_cast<const f32x4*>(V + base);
+  f32x4* Ks4 = reinterpret_cast<f32x4*>(&Ks[0][0]);
+  f32x4* Vs4 = reinterpret_cast<f32x4*>(&Vs[0][0]);
   for (int t0 = n0; t0 < n1; t0 += kTileF) {
+    f32x4 kv[NV], vv[NV];
+    float wl[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = tid + 256 * i, row = e / (D / 4), c4 = e % (D / 4);
+      const int src = min(t0 + row, n1 - 1);
+      kv[i] = K4[(size_t)src * (D / 4) + c4];
+      vv[i] = V4[(size_t)src * (D / 4) + c4];
+      wl[i] = W != nullptr ? W[(size_t)bh * N + src] : 0.f;
+    }
     __syncthreads();
-    for (int e = tid; e < kTileF * D; e += 256) {
-      const int row = e / D, col = e % D, n = t0 + row;
-      const float beta = (W != nullptr && n < n1) ? sigmoid(W[(size_t)bh * N + n]) : 1.f;
-      Ks[row][col] = n < n1 ? fmaxf(K[base + (size_t)n * D + col], 0.f) * beta : 0.f;
-      Vs[row][col] = n < n1 ? V[base + (size_t)n * D + col] : 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = tid + 256 * i, row = e / (D / 4);
+      const bool live = t0 + row < n1;
+      const float beta = W != nullptr ? sigmoid(wl[i]) : 1.f;
+      f32x4 kk, vz;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        kk[x] = live ? fmaxf(kv[i][x], 0.f) * beta : 0.f;
+        vz[x] = live ? vv[i][x] : 0.f;
+      }
+      Ks4[e] = kk;
+      Vs4[e] = vz;
     }
     __syncthreads();
     for (int n = 0; n < kTileF; ++n) {
@@ -100,16 +125,37 @@ __global__ __launch_bounds__(256) void linear_out_f32(const float* __restrict__ 
   const size_t base = (size_t)bh * N * D;
   const float* S = state + (size_t)bh * (D * D + D);
   const float* z = S + D * D;
-  for (int e = tid; e < 32 * D; e += 256) {
-    const int row = e / D, col = e % D, tok = t0 + row;
-    Qs[row][col] = tok < N ? fmaxf(Q[base + (size_t)tok * D + col], 0.f) : 0.f;
+  // unconditional 16-byte loads, as in the state pass (rows past N read row N-1)
+  constexpr int NV = 32 * D / 4 / 256;
+  {
+    const f32x4* Q4 = reinterpret_cast<const f32x4*>(Q + base);
+    f32x4 qv[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = tid + 256 * i, row = e / (D / 4), c4 = e % (D / 4);
+      qv[i] = Q4[(size_t)min(t0 + row, N - 1) * (D / 4) + c4];
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = tid + 256 * i, row = e / (D / 4);
+      f32x4 r;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) r[x] = t0 + row < N ? fmaxf(qv[i][x], 0.f) : 0.f;
+      reinterpret_cast<f32x4*>(&Qs[0][0])[e] = r;
+    }
   }
   float acc[J];
 #pragma unroll
   for (int j = 0; j < J; ++j) acc[j] = 0.f;
+  const f32x4* S4 = reinterpret_cast<const f32x4*>(S);
+#pragma unroll 1
   for (int i0 = 0; i0 < D; i0 += 32) {
+    f32x4 sv[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) sv[i] = S4[i0 * (D / 4) + tid + 256 * i];
     __syncthreads();
-    for (int e = tid; e < 32 * D; e += 256) Ss[e / D][e % D] = S[(i0 + e / D) * D + e % D];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) reinterpret_cast<f32x4*>(&Ss[0][0])[tid + 256 * i] = sv[i];
     __syncthreads();
     for (int ii = 0; ii < 32; ++ii) {
       const float a = Qs[n][i0 + ii];
@@ -118,17 +164,32 @@ __global__ __launch_bounds__(256) void linear_out_f32(const float* __restrict__ 
     }
   }
   float den = 0.f;
+#pragma unroll 8
   for (int i = 0; i < D; ++i) den = fmaf(Qs[n][i], z[i], den);
   den += eps;
   const int tok = t0 + n;
   if (tok >= N) return;
+  // J consecutive outputs: their gate (and previous output) loads go out together
+  const size_t off = base + (size_t)tok * D + jg * J;
+  const f32x4* G4 = reinterpret_cast<const f32x4*>(G + off);
+  f32x4* O4 = reinterpret_cast<f32x4*>(out + off);
+  f32x4 gv[J / 4], pv[J / 4];
 #pragma unroll
-  for (int j = 0; j < J; ++j) {
-    const size_t off = base + (size_t)tok * D + jg * J + j;
-    const float gate = 1.0f / (1.0f + expf(-G[off]));
-    float o = gate * (acc[j] / den);
-    if (accumulate) o += out[off];
-    out[off] = o;
+  for (int x = 0; x < J / 4; ++x) gv[x] = G4[x];
+  if (accumulate) {
+#pragma unroll
+    for (int x = 0; x < J / 4; ++x) pv[x] = O4[x];
+  }
+#pragma unroll
+  for (int x = 0; x < J / 4; ++x) {
+    f32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float gate = 1.0f / (1.0f + expf(-gv[x][e]));
+      o[e] = gate * (acc[4 * x + e] / den);
+    }
+    if (accumulate) o += pv[x];
+    O4[x] = o;
   }
 }
 

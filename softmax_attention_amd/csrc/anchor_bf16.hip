@@ -229,7 +229,9 @@ __global__ __launch_bounds__(kThreads, 1) void anchor_bf16(const TIn* __restrict
     goff_v[i] = ((uint32_t)vd * n_pad + ((vpc ^ vt_swz(vd)) * 8)) * 2;
   }
   const uint32_t vt_head_bytes = (uint32_t)D * n_pad * 2;
-  // issue K (or V^T) tile j into LDS buffer buf (completion: wait_all_memory + barrier)
+  // issue K (or V^T) tile j into LDS buffer buf (completion: wait_all_memory + barrier).
+  // No branch on the tile index: a tile past the end gets a zero-size descriptor,
+  // so its loads touch no memory and fill LDS with zeros that nothing reads.
   auto load_k = [&](int j, auto buf_c) {
     if (KW < kWaves && wave >= KW) return;  // wave-uniform
     const uint32_t done = (uint32_t)j * kTileBytes;
@@ -306,13 +308,6 @@ __global__ __launch_bounds__(kThreads, 1) void anchor_bf16(const TIn* __restrict
         acc[b] = mfma32x32x16(a, pb[ks], acc[b]);
       }
     }
-  };
-  // issue loads: K tile jk and V tile jv into the K and V buffers buf_c. No
-  // branch: a tile past the end gets a zero-size descriptor, so its loads
-  // touch no memory and fill LDS with zeros that nothing reads.
-  auto issue = [&](int jk, int jv, auto buf_c) {
-    load_k(jk, buf_c);
-    load_v(jv, buf_c);
   };
   // online softmax of S^T for tile j: returns the bf16 P^T operands in pb and
   // the factor alpha by which the accumulator must be rescaled (1 if none)

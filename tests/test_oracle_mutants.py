@@ -145,7 +145,9 @@ def test_correct_oracle_passes_checks():
 @pytest.mark.parametrize("mutant", [lin_no_eps, lin_gate_sign, lin_state_transposed, lin_z_wrong_axis,
                                     lin_no_relu_on_q, lin_eps_in_numerator])
 def test_linear_mutant_is_caught(mutant):
-    assert linear_checks(mutant) > 0, mutant.__name__
+    # a mutant without eps divides 0 by 0 on all-zero feature rows: expected here
+    with np.errstate(invalid="ignore", divide="ignore"):
+        assert linear_checks(mutant) > 0, mutant.__name__
 
 
 @pytest.mark.parametrize("mutant", [sm_no_scale, sm_wrong_axis, sm_no_max_sub, sm_gate_before_pv,

@@ -15,8 +15,9 @@ stack).
 --profile {anchor,linear,step,copy} runs just that piece a few times, for
 rocprofv3 kernel traces and counter passes (copy: a plain device copy of known
 size that calibrates FETCH_SIZE / WRITE_SIZE); anchor_fp8, linear_fp8 and
-step_fp8 do the same on fp8 (e4m3) copies of the inputs; attnres runs the
-block-attention-residual routing at the stack shape with two blocks.
+step_fp8 do the same on fp8 (e4m3) copies of the inputs; linear_wg runs the
+write-gated linear layer; attnres runs the block-attention-residual routing at
+the stack shape with two blocks; tiny runs the tiny fp32 pair.
 """
 from __future__ import annotations
 
@@ -88,7 +89,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--profile", default=None,
                     choices=["anchor", "linear", "step", "copy", "anchor_fp8", "linear_fp8", "step_fp8",
-                             "attnres"])
+                             "attnres", "linear_wg", "tiny"])
     ap.add_argument("--iters", type=int, default=5, help="launches per --profile run")
     ap.add_argument("--sweep", action="store_true",
                     help="720p duration sweep: one gated linear and one gated softmax layer per clip "
@@ -147,7 +148,7 @@ def cpu_baseline(w, budget_s: float):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the benchmark runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
@@ -170,6 +171,20 @@ def main():
             attnres_timing(torch, hla, reps=1)
         res = attnres_timing(torch, hla, reps=args.iters)
         print(json.dumps({"profile": "attnres", **res}))
+        return
+
+    if args.profile == "tiny":
+        # the tiny fp32 pair (B=1, H=2, N=256, D=32): one linear and one anchor call per iteration
+        from hla_inputs import BY_NAME, layer_inputs
+        wt = BY_NAME["tiny_f32"]
+        q, k, v, g = (t.to(dev) for t in layer_inputs(wt, 0))
+        out = torch.empty_like(q)
+        wsl, wsa = hla.linear_workspace(q), hla.anchor_workspace(q)
+        for _ in range(args.warmup + args.iters):
+            hla.hla_linear_fwd(q, k, v, g, out=out, eps=wt.eps, workspace=wsl)
+            hla.hla_softmax_anchor_fwd(q, k, v, g, out=out, scale=wt.scale, workspace=wsa)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile": "tiny", "workload": wt.name, "warmup": args.warmup, "iters": args.iters}))
         return
 
     if args.profile == "copy":
@@ -197,10 +212,21 @@ def main():
         q, k, v, g = sets[i % 2]
         hla.hla_softmax_anchor_fwd(q, k, v, g, out=outs[1], scale=w.scale, workspace=ws_a)
 
+    logits = None
+    if args.profile == "linear_wg":
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(20261203 + 1000 * w.index + 8)
+        logits = [torch.randn((w.B, w.H, w.N), generator=gen, device=dev).to(torch.bfloat16) for _ in range(2)]
+
+    def linear_wg(i):
+        q, k, v, g = sets[i % 2]
+        hla.hla_linear_write_gated_fwd(q, k, v, g, logits[i % 2], out=outs[0], eps=w.eps, workspace=ws)
+
     if args.profile:
         # args.warmup untimed launches first, then args.iters; a trace summary
         # drops the first args.warmup launches of each kernel
-        fn = {"anchor": [anchor], "linear": [linear], "step": [linear, anchor]}[args.profile]
+        fn = {"anchor": [anchor], "linear": [linear], "step": [linear, anchor],
+              "linear_wg": [linear_wg]}[args.profile]
         for i in range(args.warmup + args.iters):
             for f in fn:
                 f(i)

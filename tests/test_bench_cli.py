@@ -1,5 +1,5 @@
 """bench.py's command-line contract that needs no GPU: more than one GPU is
-refused with a message (this build runs on one GPU)."""
+refused with a message (the benchmark runs on one GPU)."""
 import json
 import os
 import subprocess

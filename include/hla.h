@@ -32,7 +32,8 @@
  * anchor forms Q K^T from them on the fp8 matrix cores (exact products, fp32
  * sums); everywhere else they are converted exactly to bf16 where the kernels
  * read them. Results are thus those of the bf16 path on the same values, up to
- * the fp32 summation order of Q K^T.
+ * the fp32 summation order (of Q K^T in the anchor, of phi(Q) S in the linear
+ * layer).
  *
  * Errors: every argument is checked on the host before any HIP call. On error
  * nothing is enqueued and the output is untouched. On success the work is

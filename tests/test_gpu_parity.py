@@ -317,6 +317,20 @@ def test_duration_sweep_longest_sampled():
     assert e_sm <= TOL[torch.bfloat16]
 
 
+@pytest.mark.parametrize("D", [32, 128])
+def test_hybrid_stack_fp32(D):
+    # the stack on the fp32 path (VALU kernels): delta = x4 - x0 to the fp32 bar
+    B, H, N = 1, 2, 300
+    kinds = oracle.hybrid_kinds(4)
+    layers = [make((B, H, N, D), 7500 + 10 * l + D, torch.float32) for l in range(4)]
+    x0 = custom((B, H, N, D), 7599 + D, torch.float32, n=1)[0]
+    x = x0.to(DEV)
+    hla.hla_hybrid_stack_fwd(x, [tuple(t.to(DEV) for t in L) for L in layers], kinds)
+    torch.cuda.synchronize()
+    ref = oracle.hybrid_stack(x0, layers, kinds, 1e-6, D ** -0.5) - oracle.as_f64(x0)
+    assert rel_err(x.cpu() - x0, ref) <= TOL[torch.float32]
+
+
 def test_hybrid_stack_bf16_residual_and_d64():
     # the stack with a bf16 residual stream (rounded after every layer) and with
     # head dim 64; delta = x_L - x_0 against the per-layer oracle sum

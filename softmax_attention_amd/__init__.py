@@ -152,20 +152,54 @@ def _new_out(q):
 
 
 def _check(*ts):
+    """Inputs of one call: on the GPU, on one device, contiguous, one shape, one dtype.
+
+    The C ABI takes a single in_dtype (from q) for q, k, v and g; a tensor of another
+    dtype would be read with the wrong element size, so the mismatch is refused here,
+    before any launch."""
     ref = ts[0]
     for t in ts:
         if not t.is_cuda:
             raise ValueError("tensors must live on the GPU")
+        if t.device != ref.device:
+            raise ValueError(f"tensors on different devices: {t.device} vs {ref.device}")
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous [B, H, N, D]")
         if t.shape != ref.shape:
             raise ValueError(f"shape mismatch {tuple(t.shape)} vs {tuple(ref.shape)}")
+        if t.dtype != ref.dtype:
+            raise ValueError(f"dtype mismatch {t.dtype} vs {ref.dtype}: q, k, v and g share one dtype")
 
 
-def _stream(stream) -> int:
+def _check_out(q, out):
+    """The output (or residual stream) of a call: q's shape and device, contiguous."""
+    if not out.is_cuda or out.device != q.device:
+        raise ValueError(f"out must live on q's device {q.device}")
+    if not out.is_contiguous():
+        raise ValueError("out must be contiguous [B, H, N, D]")
+    if out.shape != q.shape:
+        raise ValueError(f"shape mismatch {tuple(out.shape)} vs {tuple(q.shape)}")
+
+
+def _stream(stream, device) -> int:
+    """HIP stream handle of the call: ``stream``, or torch's current stream on ``device``."""
     torch = _torch()
-    s = torch.cuda.current_stream() if stream is None else stream
+    s = torch.cuda.current_stream(device) if stream is None else stream
     return int(s.cuda_stream)
+
+
+def _on(stream, device):
+    """Context for a call's allocations and launch: the tensors' device, and the call's
+    stream as torch's current stream, so that a workspace or output allocated here
+    belongs to the stream that uses it (the caching allocator hands a freed block only
+    to later work on the same stream)."""
+    import contextlib
+    torch = _torch()
+    ctx = contextlib.ExitStack()
+    ctx.enter_context(torch.cuda.device(device))
+    if stream is not None:
+        ctx.enter_context(torch.cuda.stream(stream))
+    return ctx
 
 
 def _raise(fn: str, st: int):
@@ -210,20 +244,30 @@ def stack_workspace(q, kinds, out_dtype=None):
     return _workspace(n, q.device)
 
 
+def _workspace_check(workspace, q):
+    if not workspace.is_cuda or workspace.device != q.device:
+        raise ValueError(f"workspace must live on q's device {q.device}")
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+
+
 def hla_linear_fwd(q, k, v, g, out=None, accumulate: bool = False, eps: float = 1e-6,
                    workspace=None, stream=None):
     """Gated linear attention O = sigma(G) * (phi(Q) S) / (phi(Q) z + eps); returns out."""
-    torch = _torch()
     _check(q, k, v, g)
-    if out is None:
-        out = _new_out(q)
-    _check(q, out)
-    d = dims_of(q, out.dtype)
-    if workspace is None:
-        workspace = linear_workspace(q, out.dtype)
-    st = lib.hla_linear_fwd(ctypes.byref(d), q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(),
-                            out.data_ptr(), int(bool(accumulate)), float(eps), workspace.data_ptr(),
-                            workspace.numel() * workspace.element_size(), _stream(stream))
+    if out is not None:
+        _check_out(q, out)
+    with _on(stream, q.device):
+        if out is None:
+            out = _new_out(q)
+        d = dims_of(q, out.dtype)
+        if workspace is None:
+            workspace = linear_workspace(q, out.dtype)
+        _workspace_check(workspace, q)
+        st = lib.hla_linear_fwd(ctypes.byref(d), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                g.data_ptr(), out.data_ptr(), int(bool(accumulate)), float(eps),
+                                workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                _stream(stream, q.device))
     _raise("hla_linear_fwd", st)
     return out
 
@@ -233,23 +277,26 @@ def hla_linear_write_gated_fwd(q, k, v, g, w, out=None, accumulate: bool = False
     """Write-gated linear attention: token n enters the state with sigma(w_n); returns out.
 
     w has shape [B, H, N] and the dtype of q."""
-    torch = _torch()
     _check(q, k, v, g)
     if tuple(w.shape) != tuple(q.shape[:-1]) or w.dtype != q.dtype or not w.is_contiguous():
         raise ValueError("w must be a contiguous [B, H, N] tensor of q's dtype")
-    if not w.is_cuda:
-        raise ValueError("tensors must live on the GPU")
-    if out is None:
-        out = _new_out(q)
-    _check(q, out)
-    d = dims_of(q, out.dtype)
-    if workspace is None:
-        workspace = linear_workspace(q, out.dtype)
-    st = lib.hla_linear_write_gated_fwd(ctypes.byref(d), q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                                        g.data_ptr(), w.data_ptr(), out.data_ptr(),
-                                        int(bool(accumulate)), float(eps), workspace.data_ptr(),
-                                        workspace.numel() * workspace.element_size(),
-                                        _stream(stream))
+    if not w.is_cuda or w.device != q.device:
+        raise ValueError(f"w must live on q's device {q.device}")
+    if out is not None:
+        _check_out(q, out)
+    with _on(stream, q.device):
+        if out is None:
+            out = _new_out(q)
+        d = dims_of(q, out.dtype)
+        if workspace is None:
+            workspace = linear_workspace(q, out.dtype)
+        _workspace_check(workspace, q)
+        st = lib.hla_linear_write_gated_fwd(ctypes.byref(d), q.data_ptr(), k.data_ptr(),
+                                            v.data_ptr(), g.data_ptr(), w.data_ptr(),
+                                            out.data_ptr(), int(bool(accumulate)), float(eps),
+                                            workspace.data_ptr(),
+                                            workspace.numel() * workspace.element_size(),
+                                            _stream(stream, q.device))
     _raise("hla_linear_write_gated_fwd", st)
     return out
 
@@ -257,47 +304,56 @@ def hla_linear_write_gated_fwd(q, k, v, g, w, out=None, accumulate: bool = False
 def hla_softmax_anchor_fwd(q, k, v, g, out=None, accumulate: bool = False,
                            scale: Optional[float] = None, workspace=None, stream=None):
     """Gated softmax anchor O = sigma(G) * softmax(scale Q K^T) V; returns out."""
-    torch = _torch()
     _check(q, k, v, g)
-    if out is None:
-        out = _new_out(q)
-    _check(q, out)
-    d = dims_of(q, out.dtype)
     scale = 1.0 / math.sqrt(q.shape[-1]) if scale is None else float(scale)
-    if workspace is None:
-        workspace = anchor_workspace(q, out.dtype)
-    st = lib.hla_softmax_anchor_fwd(ctypes.byref(d), q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                                    g.data_ptr(), out.data_ptr(), int(bool(accumulate)), scale,
-                                    workspace.data_ptr(),
-                                    workspace.numel() * workspace.element_size(), _stream(stream))
+    if out is not None:
+        _check_out(q, out)
+    with _on(stream, q.device):
+        if out is None:
+            out = _new_out(q)
+        d = dims_of(q, out.dtype)
+        if workspace is None:
+            workspace = anchor_workspace(q, out.dtype)
+        _workspace_check(workspace, q)
+        st = lib.hla_softmax_anchor_fwd(ctypes.byref(d), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                        g.data_ptr(), out.data_ptr(), int(bool(accumulate)), scale,
+                                        workspace.data_ptr(),
+                                        workspace.numel() * workspace.element_size(),
+                                        _stream(stream, q.device))
     _raise("hla_softmax_anchor_fwd", st)
     return out
 
 
 def hla_hybrid_stack_fwd(x, layers: Sequence, kinds: Sequence[int], eps: float = 1e-6,
                          scale: Optional[float] = None, workspace=None, stream=None):
-    """x += layer_l(q_l, k_l, v_l, g_l) for each layer in order (in place); returns x."""
+    """x += layer_l(q_l, k_l, v_l, g_l) for each layer in order (in place); returns x.
+
+    Every layer's q, k, v, g share the shape, dtype and device of layer 0's q."""
     n = len(layers)
     if n != len(kinds):
         raise ValueError("layers and kinds differ in length")
-    for (q, k, v, g) in layers:
-        _check(q, k, v, g)
-        _check(q, x)
+    if n == 0:
+        raise ValueError("the stack needs at least one layer")
     q0 = layers[0][0]
-    d = dims_of(q0, x.dtype)
+    for (q, k, v, g) in layers:
+        _check(q0, q, k, v, g)
+    _check_out(q0, x)
     scale = 1.0 / math.sqrt(q0.shape[-1]) if scale is None else float(scale)
-    if workspace is None:
-        workspace = stack_workspace(q0, kinds, x.dtype)
-    arr = ctypes.c_void_p * n
-    qs = arr(*[l[0].data_ptr() for l in layers])
-    ks = arr(*[l[1].data_ptr() for l in layers])
-    vs = arr(*[l[2].data_ptr() for l in layers])
-    gs = arr(*[l[3].data_ptr() for l in layers])
-    kd = (ctypes.c_int32 * n)(*[int(x_) for x_ in kinds])
-    wp = workspace.data_ptr() if workspace is not None else None
-    wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = lib.hla_hybrid_stack_fwd(ctypes.byref(d), n, kd, qs, ks, vs, gs, x.data_ptr(), float(eps),
-                                  scale, wp, wb, _stream(stream))
+    with _on(stream, q0.device):
+        d = dims_of(q0, x.dtype)
+        if workspace is None:
+            workspace = stack_workspace(q0, kinds, x.dtype)
+        _workspace_check(workspace, q0)
+        arr = ctypes.c_void_p * n
+        qs = arr(*[l[0].data_ptr() for l in layers])
+        ks = arr(*[l[1].data_ptr() for l in layers])
+        vs = arr(*[l[2].data_ptr() for l in layers])
+        gs = arr(*[l[3].data_ptr() for l in layers])
+        kd = (ctypes.c_int32 * n)(*[int(x_) for x_ in kinds])
+        st = lib.hla_hybrid_stack_fwd(ctypes.byref(d), n, kd, qs, ks, vs, gs, x.data_ptr(),
+                                      float(eps), scale, workspace.data_ptr(),
+                                      workspace.numel() * workspace.element_size(),
+                                      _stream(stream, q0.device))
     _raise("hla_hybrid_stack_fwd", st)
     return x
 
@@ -310,18 +366,23 @@ def hla_attnres_route_fwd(x, summaries: Sequence, w, out=None, stream=None):
     in place)."""
     torch = _torch()
     _check(x, *summaries)
-    if x.dtype != torch.float32 or any(s_.dtype != torch.float32 for s_ in summaries):
+    if x.dtype != torch.float32:
         raise ValueError("x and the summaries must be fp32")
     D = int(x.shape[-1])
-    if tuple(w.shape) != (D, D) or w.dtype != torch.bfloat16 or not w.is_contiguous() or not w.is_cuda:
-        raise ValueError("w must be a contiguous bf16 [D, D] tensor on the GPU")
-    if out is None:
-        out = torch.empty_like(x)
-    _check(x, out)
-    d = dims_of(x, out.dtype)
-    n = len(summaries)
-    arr = (ctypes.c_void_p * max(n, 1))(*[s_.data_ptr() for s_ in summaries])
-    st = lib.hla_attnres_route_fwd(ctypes.byref(d), n, arr, x.data_ptr(), w.data_ptr(),
-                                   out.data_ptr(), _stream(stream))
+    if (tuple(w.shape) != (D, D) or w.dtype != torch.bfloat16 or not w.is_contiguous()
+            or not w.is_cuda or w.device != x.device):
+        raise ValueError("w must be a contiguous bf16 [D, D] tensor on x's device")
+    if out is not None:
+        _check_out(x, out)
+        if out.dtype != torch.float32:
+            raise ValueError("out must be fp32")
+    with _on(stream, x.device):
+        if out is None:
+            out = torch.empty_like(x)
+        d = dims_of(x, out.dtype)
+        n = len(summaries)
+        arr = (ctypes.c_void_p * max(n, 1))(*[s_.data_ptr() for s_ in summaries])
+        st = lib.hla_attnres_route_fwd(ctypes.byref(d), n, arr, x.data_ptr(), w.data_ptr(),
+                                       out.data_ptr(), _stream(stream, x.device))
     _raise("hla_attnres_route_fwd", st)
     return out

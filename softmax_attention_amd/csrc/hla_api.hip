@@ -5,23 +5,10 @@
 // runs without a GPU. Valid calls enqueue kernels on the caller's stream and
 // return without synchronising.
 #include <math.h>
-#include <stdlib.h>
 
 #include "hla_internal.h"
 
 namespace hla {
-
-// Work-split overrides for tuning sweeps, read once from the environment
-// (HLA_LINEAR_CHUNKS, HLA_LINEAR_OUT_WGS); unset or 0 keeps the built-in choice.
-Tuning& tuning() {
-  static Tuning t = [] {
-    Tuning x;
-    if (const char* e = getenv("HLA_LINEAR_CHUNKS")) x.linear_chunks = atoi(e);
-    if (const char* e = getenv("HLA_LINEAR_OUT_WGS")) x.linear_out_wgs = atoi(e);
-    return x;
-  }();
-  return t;
-}
 
 namespace {
 
@@ -80,7 +67,7 @@ LinearPlan linear_plan(const hla_dims& d) {
   if (BH <= 0 || N <= 0) return p;
   // state pass: aim at ~512 workgroups (two per CU) with chunks of >= 64 tokens
   const int64_t max_c = (N + 63) / 64;
-  int64_t c = tuning().linear_chunks > 0 ? tuning().linear_chunks : (512 + BH - 1) / BH;
+  int64_t c = kLinearChunksOverride > 0 ? kLinearChunksOverride : (512 + BH - 1) / BH;
   c = c < 1 ? 1 : (c > max_c ? max_c : c);
   int64_t T = (N + c - 1) / c;
   T = (T + 63) / 64 * 64;
@@ -88,7 +75,7 @@ LinearPlan linear_plan(const hla_dims& d) {
   p.C = int(c);
   p.T = int(T);
   // output pass: workgroups per head
-  int64_t P = tuning().linear_out_wgs > 0 ? tuning().linear_out_wgs : (512 + BH - 1) / BH;
+  int64_t P = kLinearOutWgsOverride > 0 ? kLinearOutWgsOverride : (512 + BH - 1) / BH;
   const int64_t max_p = (N + 63) / 64;
   P = P < 1 ? 1 : (P > max_p ? max_p : P);
   p.P = int(P);

@@ -22,12 +22,17 @@ struct LinearPlan {
 
 LinearPlan linear_plan(const hla_dims& d);
 
-// Work-split overrides (for sweeps); 0 keeps the built-in choice.
-struct Tuning {
-  int linear_chunks = 0;      // C override
-  int linear_out_wgs = 0;     // P override
-};
-Tuning& tuning();
+// Work-split overrides for tuning sweeps, fixed when the library is compiled
+// (-DHLA_LINEAR_CHUNKS=C, -DHLA_LINEAR_OUT_WGS=P); 0 keeps the built-in choice.
+// Nothing read at run time changes the split, so equal calls sum in equal order.
+#ifndef HLA_LINEAR_CHUNKS
+#define HLA_LINEAR_CHUNKS 0
+#endif
+#ifndef HLA_LINEAR_OUT_WGS
+#define HLA_LINEAR_OUT_WGS 0
+#endif
+constexpr int kLinearChunksOverride = HLA_LINEAR_CHUNKS;  // C override
+constexpr int kLinearOutWgsOverride = HLA_LINEAR_OUT_WGS;  // P override
 
 // w: write-gate logits [B,H,N] (in_dtype) for the write-gated variant, or NULL
 hipError_t launch_linear_bf16(const hla_dims& d, const void* q, const void* k, const void* v,

@@ -313,3 +313,58 @@ def test_one_hip_runtime_whatever_the_import_order():
     res = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr
     assert res.stdout.strip().endswith("1")
+
+
+class _FakeGpuTensor:
+    """Stands in for a device tensor in the binding's argument checks (no GPU here).
+
+    Only the attributes the checks read are present; a call that got past the
+    checks would fail on data_ptr(), which this object does not have."""
+
+    def __init__(self, shape, dtype, device="cuda:0", contiguous=True):
+        import torch
+        self.shape = torch.Size(shape)
+        self.dtype = dtype
+        self.device = torch.device(device)
+        self.is_cuda = self.device.type == "cuda"
+        self._contiguous = contiguous
+
+    def is_contiguous(self):
+        return self._contiguous
+
+
+def test_binding_rejects_mixed_dtypes_and_devices_before_any_launch(monkeypatch):
+    import torch
+    called = []
+    for fn in ("hla_linear_fwd", "hla_softmax_anchor_fwd", "hla_hybrid_stack_fwd",
+               "hla_linear_write_gated_fwd"):
+        monkeypatch.setattr(hla.lib, fn, lambda *a, _fn=fn: called.append(_fn) or 0)
+    shape = (1, 2, 64, 128)
+    bf = lambda **kw: _FakeGpuTensor(shape, torch.bfloat16, **kw)
+    f32 = _FakeGpuTensor(shape, torch.float32)
+    f8 = _FakeGpuTensor(shape, torch.float8_e4m3fn)
+    other_dev = bf(device="cuda:1")
+    # q's dtype fixes the element size the kernels read k, v and g with
+    for args in [(f32, bf(), bf(), bf()), (bf(), f32, bf(), bf()), (bf(), bf(), f8, bf()),
+                 (bf(), bf(), bf(), f32), (bf(), other_dev, bf(), bf()),
+                 (bf(), bf(), bf(contiguous=False), bf())]:
+        for call in (hla.hla_linear_fwd, hla.hla_softmax_anchor_fwd):
+            with pytest.raises(ValueError):
+                call(*args, out=bf())
+    with pytest.raises(ValueError):
+        hla.hla_linear_write_gated_fwd(bf(), bf(), bf(), bf(),
+                                       _FakeGpuTensor(shape[:-1], torch.float32), out=bf())
+    # the output: q's device, shape and contiguity
+    for out in (bf(device="cuda:1"), _FakeGpuTensor((1, 2, 63, 128), torch.bfloat16),
+                bf(contiguous=False)):
+        with pytest.raises(ValueError):
+            hla.hla_softmax_anchor_fwd(bf(), bf(), bf(), bf(), out=out)
+    # every layer of a stack shares layer 0's dtype, shape and device
+    good = (bf(), bf(), bf(), bf())
+    x = _FakeGpuTensor(shape, torch.float32)
+    for bad in [(f32, f32, f32, f32), (bf(), bf(), f8, bf()), (bf(), bf(), bf(), other_dev)]:
+        with pytest.raises(ValueError):
+            hla.hla_hybrid_stack_fwd(x, [good, bad], [0, 1])
+    with pytest.raises(ValueError):
+        hla.hla_hybrid_stack_fwd(x, [], [])
+    assert called == []

@@ -678,3 +678,49 @@ def test_concurrent_calls_on_two_streams():
         assert torch.equal(out_l, ref_l)
         assert torch.equal(out_a, ref_a)
         assert torch.equal(out_l2, ref_l2)
+
+
+def test_explicit_stream_argument_with_default_workspace():
+    # stream= passed explicitly, no workspace and no out: the binding allocates both
+    # for that stream, so a block freed after the call is not handed to other work
+    # while the kernels may still use it; results equal the current-stream call's
+    B, H, N, D = 2, 4, 2500, 128
+    q, k, v, g = (t.to(DEV) for t in make((B, H, N, D), 9600, torch.bfloat16))
+    x0 = custom((B, H, N, D), 9601, torch.float32, n=1)[0].to(DEV)
+    ref_l = hla.hla_linear_fwd(q, k, v, g)
+    ref_a = hla.hla_softmax_anchor_fwd(q, k, v, g)
+    ref_x = hla.hla_hybrid_stack_fwd(x0.clone(), [(q, k, v, g)] * 4, [0, 0, 0, 1])
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    for rep in range(3):
+        # the current stream keeps allocating and writing meanwhile
+        junk = [torch.full((B, H, N, D), float(rep + 1), device=DEV) for _ in range(3)]
+        got_l = hla.hla_linear_fwd(q, k, v, g, stream=s)
+        got_a = hla.hla_softmax_anchor_fwd(q, k, v, g, stream=s)
+        x = x0.clone()
+        torch.cuda.current_stream().synchronize()
+        hla.hla_hybrid_stack_fwd(x, [(q, k, v, g)] * 4, [0, 0, 0, 1], stream=s)
+        junk += [torch.full((B, H, N, D), -1.0, device=DEV) for _ in range(3)]
+        s.synchronize()
+        assert torch.equal(got_l, ref_l)
+        assert torch.equal(got_a, ref_a)
+        assert torch.equal(x, ref_x)
+        del junk
+
+
+def test_binding_refuses_mixed_dtypes_on_the_gpu():
+    # q's dtype fixes the element size the kernels read k, v and g with: a
+    # mismatch is refused before any launch and the output stays untouched
+    q, k, v, g = (t.to(DEV) for t in make((1, 2, 200, 128), 9700, torch.bfloat16))
+    out = torch.full(q.shape, 7.0, dtype=torch.bfloat16, device=DEV)
+    for args in [(q.float(), k, v, g), (q, k.float(), v, g), (q, k, v.to(FP8), g),
+                 (q, k, v, g.float())]:
+        for call in (hla.hla_linear_fwd, hla.hla_softmax_anchor_fwd):
+            with pytest.raises(ValueError):
+                call(*args, out=out)
+    x = torch.zeros(q.shape, device=DEV)
+    with pytest.raises(ValueError):
+        hla.hla_hybrid_stack_fwd(x, [(q, k, v, g), (q.float(), k.float(), v.float(), g.float())],
+                                 [0, 1])
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all()) and bool((x == 0).all())

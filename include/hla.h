@@ -104,6 +104,24 @@ hla_status hla_linear_fwd(const hla_dims* d, const void* q, const void* k, const
                           const void* g, void* out, int accumulate, float eps, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/* Allocation-free variant of hla_linear_fwd, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid it): same operator, arguments and results as hla_linear_fwd, but the
+ * partial states and reduced state live in a scratch array of
+ * HLA_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on (from
+ * the module load until the process ends); no workspace argument, and the call
+ * allocates nothing. Returns HLA_ERR_WORKSPACE, enqueuing nothing, when the call
+ * would need more than that (hla_linear_workspace_bytes(d) above the limit), and
+ * HLA_ERR_HIP if the scratch array's address cannot be found on the current
+ * device (looked up once per device, on the first call there). The array's
+ * contents on entry do not matter. Calls on one GPU share that GPU's array:
+ * calls that overlap in time on one GPU (concurrent streams, or threads) race
+ * and give undefined results; order them on one stream. */
+#define HLA_NOALLOC_SCRATCH_BYTES (64u << 20)
+hla_status hla_linear_fwd_noalloc(const hla_dims* d, const void* q, const void* k, const void* v,
+                                  const void* g, void* out, int accumulate, float eps,
+                                  void* stream);
+
 /* Write-gated linear attention: as hla_linear_fwd, but each token writes into the
  * state with strength beta_n = sigma(W_n), one logit per token and head:
  *   S = sum_n beta_n phi(K_n)^T V_n,  z = sum_n beta_n phi(K_n)

@@ -29,7 +29,7 @@ STATUS = {
     4: "HLA_ERR_BAD_ARG", 5: "HLA_ERR_ALIGN", 6: "HLA_ERR_WORKSPACE", 7: "HLA_ERR_HIP",
 }
 EXPORTS = ("hla_abi_version", "hla_status_str", "hla_linear_workspace_bytes", "hla_linear_fwd",
-           "hla_linear_write_gated_fwd", "hla_softmax_anchor_workspace_bytes",
+           "hla_linear_fwd_noalloc", "hla_linear_write_gated_fwd", "hla_softmax_anchor_workspace_bytes",
            "hla_softmax_anchor_fwd", "hla_hybrid_stack_fwd", "hla_attnres_route_fwd")
 
 
@@ -78,6 +78,8 @@ def _load() -> ctypes.CDLL:
     lib.hla_linear_fwd.restype = ctypes.c_int
     lib.hla_linear_fwd.argtypes = [pd, P, P, P, P, P, ctypes.c_int, ctypes.c_float, P,
                                    ctypes.c_size_t, P]
+    lib.hla_linear_fwd_noalloc.restype = ctypes.c_int
+    lib.hla_linear_fwd_noalloc.argtypes = [pd, P, P, P, P, P, ctypes.c_int, ctypes.c_float, P]
     lib.hla_linear_write_gated_fwd.restype = ctypes.c_int
     lib.hla_linear_write_gated_fwd.argtypes = [pd, P, P, P, P, P, P, ctypes.c_int, ctypes.c_float,
                                                P, ctypes.c_size_t, P]
@@ -269,6 +271,24 @@ def hla_linear_fwd(q, k, v, g, out=None, accumulate: bool = False, eps: float = 
                                 workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                 _stream(stream, q.device))
     _raise("hla_linear_fwd", st)
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # HLA_NOALLOC_SCRATCH_BYTES of include/hla.h
+
+
+def hla_linear_fwd_noalloc(q, k, v, g, out, accumulate: bool = False, eps: float = 1e-6,
+                           stream=None):
+    """hla_linear_fwd without a workspace: the library's per-GPU scratch array holds
+    the partial states. The caller passes the output; nothing is allocated."""
+    _check(q, k, v, g)
+    _check_out(q, out)
+    with _on(stream, q.device):
+        d = dims_of(q, out.dtype)
+        st = lib.hla_linear_fwd_noalloc(ctypes.byref(d), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                        g.data_ptr(), out.data_ptr(), int(bool(accumulate)),
+                                        float(eps), _stream(stream, q.device))
+    _raise("hla_linear_fwd_noalloc", st)
     return out
 
 

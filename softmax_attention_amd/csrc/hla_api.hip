@@ -6,6 +6,8 @@
 // return without synchronising.
 #include <math.h>
 
+#include <mutex>
+
 #include "hla_internal.h"
 
 namespace hla {
@@ -122,6 +124,35 @@ static hla_status linear_common(const hla_dims* d, const void* q, const void* k,
   return from_hip(launch_linear_f32(*d, q, k, v, g, w, out, accumulate, eps, workspace, plan, s));
 }
 
+// Scratch memory of the allocation-free linear entry point: one copy per GPU
+// (each device that loads the library holds it until the process ends). The
+// array's name is a host-side stand-in in host code; kernels get the device
+// address that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[HLA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_ptr[kMaxDevices];  // device address of `scratch`, per device
+
+// Address of the current device's scratch array, looked up once per device.
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return hipSuccess;
+}
+}  // namespace
+
 extern "C" {
 
 int hla_abi_version(void) { return HLA_ABI_VERSION; }
@@ -155,6 +186,22 @@ hla_status hla_linear_fwd(const hla_dims* d, const void* q, const void* k, const
                           size_t workspace_bytes, void* stream) {
   return linear_common(d, q, k, v, g, nullptr, false, out, accumulate, eps, workspace,
                        workspace_bytes, stream);
+}
+
+hla_status hla_linear_fwd_noalloc(const hla_dims* d, const void* q, const void* k, const void* v,
+                                  const void* g, void* out, int accumulate, float eps,
+                                  void* stream) {
+  hla_status st = check_dims(d);
+  if (st != HLA_OK) return st;
+  if (!isfinite(eps) || eps < 0.f || (accumulate != 0 && accumulate != 1)) return HLA_ERR_BAD_ARG;
+  if (empty(d)) return HLA_OK;
+  if ((st = check_tensors(q, k, v, g, out)) != HLA_OK) return st;
+  if (linear_plan(*d).total > size_t(HLA_NOALLOC_SCRATCH_BYTES)) return HLA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  clear_pending_error();
+  if (scratch_address(&ws) != hipSuccess) return HLA_ERR_HIP;
+  return linear_common(d, q, k, v, g, nullptr, false, out, accumulate, eps, ws,
+                       HLA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 hla_status hla_linear_write_gated_fwd(const hla_dims* d, const void* q, const void* k,

@@ -368,3 +368,24 @@ def test_binding_rejects_mixed_dtypes_and_devices_before_any_launch(monkeypatch)
     with pytest.raises(ValueError):
         hla.hla_hybrid_stack_fwd(x, [], [])
     assert called == []
+
+
+def test_noalloc_argument_errors():
+    # validated on the host before any HIP call, like the other entry points
+    def call(d, q=FAKE, k=FAKE, v=FAKE, g=FAKE, out=FAKE, acc=0, eps=1e-6):
+        return hla.lib.hla_linear_fwd_noalloc(ctypes.byref(d) if d is not None else None,
+                                              q, k, v, g, out, acc, eps, None)
+    assert call(None) == NULLP
+    assert call(dims(D=96)) == UNSUP
+    assert call(dims(N=-1)) == SHAPE
+    assert call(dims(), eps=-1.0) == BADARG
+    assert call(dims(), acc=2) == BADARG
+    assert call(dims(), q=None) == NULLP
+    assert call(dims(), out=ODD) == ALIGN
+    assert call(dims(N=0), q=None, k=None, v=None, g=None, out=None) == OK
+    # more than the scratch array holds: refused before any GPU work
+    big = dims(B=1, H=4000, N=4096, D=128)
+    assert hla.hla_linear_workspace_bytes(big) > hla.NOALLOC_SCRATCH_BYTES
+    assert call(big) == WS
+    fits = dims(B=2, H=16, N=19320, D=128)
+    assert hla.hla_linear_workspace_bytes(fits) <= hla.NOALLOC_SCRATCH_BYTES

@@ -148,6 +148,17 @@ __device__ __forceinline__ f32x4 fp8x4_to_f32(uint32_t w) {
 __device__ __forceinline__ float fp8_to_f32(uint8_t b) {
   return __builtin_amdgcn_cvt_pk_f32_fp8((uint32_t)b, false)[0];
 }
+// ReLU on four packed e4m3 values: a byte is negative exactly when its top
+// bit is set. v_perm_b32 selectors 8-11 yield 0xff or 0x00 from the top bit
+// of bytes 1, 3, 5 and 7 of {first operand : second operand}; with x << 8 as
+// the first operand those are the sign bits of x's bytes 0 and 2, with x as
+// the second, of bytes 1 and 3. The mask then clears every negative byte
+// (-0 included; a NaN with the sign bit set becomes 0, as the bf16 route does).
+__device__ __forceinline__ uint32_t relu_fp8x4(uint32_t x) {
+  const uint32_t neg = __builtin_amdgcn_perm(x << 8, x, 0x090B080Au);
+  return x & ~neg;
+}
+
 // eight fp8 values (8 bytes) -> eight bf16 (one 16-byte MFMA operand), exact:
 // v_cvt_scalef32_pk_bf16_fp8 with scale 1 converts two values per instruction
 // (every e4m3 value is a bf16 value; checked equal to the fp32 route on all

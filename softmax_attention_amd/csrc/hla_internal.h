@@ -33,6 +33,16 @@ LinearPlan linear_plan(const hla_dims& d);
 #endif
 constexpr int kLinearChunksOverride = HLA_LINEAR_CHUNKS;  // C override
 constexpr int kLinearOutWgsOverride = HLA_LINEAR_OUT_WGS;  // P override
+// Token groups each output-pass wave keeps in flight ahead of the one it
+// computes, for bf16 and for fp8 inputs.
+#ifndef HLA_LINEAR_OUT_PREFETCH
+#define HLA_LINEAR_OUT_PREFETCH 2
+#endif
+#ifndef HLA_LINEAR_OUT_PREFETCH_F8
+#define HLA_LINEAR_OUT_PREFETCH_F8 2
+#endif
+constexpr int kLinearOutPrefetch = HLA_LINEAR_OUT_PREFETCH;
+constexpr int kLinearOutPrefetchF8 = HLA_LINEAR_OUT_PREFETCH_F8;
 
 // w: write-gate logits [B,H,N] (in_dtype) for the write-gated variant, or NULL
 hipError_t launch_linear_bf16(const hla_dims& d, const void* q, const void* k, const void* v,

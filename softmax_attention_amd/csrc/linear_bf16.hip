@@ -115,6 +115,28 @@ __device__ __forceinline__ void transpose8x8(const u32x4* in, u32x4* out) {
   }
 }
 
+// A wave's quadrant of a chunk's partial S, stored in the output pass's
+// fragment order (bf16, see frag_pos) so the reduce reads and writes whole
+// fragments contiguously. C-tile element (q*4 + e) of lane (col r, half h2) is
+// row q*8 + 4h2 + e: 4 consecutive slots.
+template <int D, bool F8, int RB>
+__device__ __forceinline__ void store_partial_s(const f32x16 (&acc)[RB][RB], char* Pc, int ib0,
+                                                int jb0, int lane) {
+  uint16_t* PS = reinterpret_cast<uint16_t*>(Pc);
+  const int r = lane & 31, h2 = lane >> 5;
+#pragma unroll
+  for (int x = 0; x < RB; ++x)
+#pragma unroll
+    for (int y = 0; y < RB; ++y)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int row = (ib0 + x) * 32 + 8 * q + 4 * h2, col = (jb0 + y) * 32 + r;
+        *reinterpret_cast<u32x2*>(&PS[frag_pos<D, F8>(row, col)]) =
+            (u32x2){pack_bf16(acc[x][y][q * 4], acc[x][y][q * 4 + 1]),
+                    pack_bf16(acc[x][y][q * 4 + 2], acc[x][y][q * 4 + 3])};
+      }
+}
+
 template <int D, bool WG, typename TIn>
 __global__ __launch_bounds__(256) void linear_state_bf16(const TIn* __restrict__ K,
                                                          const TIn* __restrict__ V,
@@ -229,23 +251,9 @@ __global__ __launch_bounds__(256) void linear_state_bf16(const TIn* __restrict__
     }
   }
 
-  // partial S, stored in the output pass's fragment order (bf16, see frag_pos)
-  // so the reduce reads and writes whole fragments contiguously. C-tile element
-  // (q*4 + e) of lane (col r, half h2) is row q*8 + 4h2 + e: 4 consecutive slots.
   char* Pc = part + ((size_t)bh * C + c) * Partial<D>::kBytes;
-  uint16_t* PS = reinterpret_cast<uint16_t*>(Pc);
   float* Pz = reinterpret_cast<float*>(Pc + Partial<D>::kSBytes);
-#pragma unroll
-  for (int x = 0; x < RB; ++x)
-#pragma unroll
-    for (int y = 0; y < RB; ++y)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int row = (ib0 + x) * 32 + 8 * q + 4 * h2, col = (jb0 + y) * 32 + r;
-        *reinterpret_cast<u32x2*>(&PS[frag_pos<D, F8>(row, col)]) =
-            (u32x2){pack_bf16(acc[x][y][q * 4], acc[x][y][q * 4 + 1]),
-                    pack_bf16(acc[x][y][q * 4 + 2], acc[x][y][q * 4 + 3])};
-      }
+  store_partial_s<D, F8, RB>(acc, Pc, ib0, jb0, lane);
 
   // partial z: the K thread of block (fc, tg) holds features fc*EPL .. +EPL over
   // its token groups; sum the TG groups of each feature in a fixed order
@@ -260,6 +268,135 @@ __global__ __launch_bounds__(256) void linear_state_bf16(const TIn* __restrict__
     float sum = 0.f;
     for (int g = 0; g < TG; ++g) sum += zred[g * D + tid];
     Pz[tid] = sum;
+  }
+}
+
+// fp8 inputs without a write gate: the tiles stay e4m3 and the contraction runs
+// on the 32x32x64 fp8 matrix instruction (products exact in fp32, fp32 sums),
+// so a tile costs the LDS bytes and matrix-core cycles of a bf16 tile of half
+// as many tokens. Same block scheme as linear_state_bf16: each thread loads an
+// 8-token x 16-feature block, clears negative K bytes (phi), and transposes it
+// with byte permutes into 16 feature rows of 8 tokens; an A or B operand (32
+// consecutive tokens of one feature) is then two 16-byte LDS reads. z = phi(K)^T 1
+// comes from the same instruction with a B operand of ones (e4m3 1.0 = 0x38),
+// on the two waves whose quadrant starts at column 0.
+template <int D>
+__global__ __launch_bounds__(256) void linear_state_fp8(const uint8_t* __restrict__ K,
+                                                        const uint8_t* __restrict__ V,
+                                                        char* __restrict__ part, int N, int T,
+                                                        int C) {
+  constexpr int FC = D / 16;    // 16-feature chunks per token row
+  constexpr int TG = 128 / FC;  // 8-token groups per tile: one block per thread and tensor
+  constexpr int TILE = 8 * TG;  // tokens per tile (one byte each per feature row)
+  constexpr int CH = TILE / 16; // 16-byte chunks per feature row
+  constexpr int RB = D / 64;    // 32-wide blocks per wave per side
+  __shared__ __attribute__((aligned(16))) uint8_t Kt[D * TILE];
+  __shared__ __attribute__((aligned(16))) uint8_t Vt[D * TILE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = blockIdx.x, bh = blockIdx.y;
+  const int n0 = c * T;
+  const int n1 = min(N, n0 + T);
+  const size_t base = (size_t)bh * N * D;
+  const bool isk = tid < 128;  // waves 0-1: K blocks, waves 2-3: V blocks
+  const int jb = tid & 127, fc = jb % FC, tg = jb / FC;
+  const uint8_t* src = (isk ? K : V) + base + fc * 16;
+  uint8_t* tile = isk ? Kt : Vt;
+
+  u32x4 raw[8];  // tokens 8tg .. 8tg+7 of the tile, features 16fc .. +15
+  f32x16 acc[RB][RB], zacc[RB];
+#pragma unroll
+  for (int x = 0; x < RB; ++x) {
+    zacc[x] = (f32x16){};
+#pragma unroll
+    for (int y = 0; y < RB; ++y) acc[x][y] = (f32x16){};
+  }
+  auto load_tile = [&](int t0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int n = t0 + 8 * tg + i;
+      raw[i] = n < n1 ? ldg16_stream(src + (size_t)n * D) : (u32x4){0, 0, 0, 0};
+    }
+  };
+  auto lds_chunk = [&](const uint8_t* t, int row, int lc) {
+    return *reinterpret_cast<const u32x4*>(&t[row * TILE + ((lc ^ t_swz<CH>(row)) * 16)]);
+  };
+
+  const int r = lane & 31, h2 = lane >> 5;
+  const int ib0 = (wave >> 1) * RB, jb0 = (wave & 1) * RB;
+  const bool zwave = (wave & 1) == 0;
+  const u32x8 ones = {0x38383838u, 0x38383838u, 0x38383838u, 0x38383838u,
+                      0x38383838u, 0x38383838u, 0x38383838u, 0x38383838u};
+  const int ntiles = (n1 - n0 + TILE - 1) / TILE;
+
+  load_tile(n0);
+  for (int it = 0; it < ntiles; ++it) {
+    __syncthreads();  // every wave is done reading the previous tile
+    if (isk) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) raw[i][d] = relu_fp8x4(raw[i][d]);
+    }
+    // 4 x 4 byte transposes: dword d of tokens 4th .. 4th+3 -> features
+    // 4d .. 4d+3, four tokens each (v_perm_b32 takes bytes 0-3 from its second
+    // operand and 4-7 from its first)
+    uint32_t cols[16][2];
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int th = 0; th < 2; ++th) {
+        const int i0 = 4 * th;
+        const uint32_t a = __builtin_amdgcn_perm(raw[i0 + 1][d], raw[i0][d], 0x05010400u);
+        const uint32_t b = __builtin_amdgcn_perm(raw[i0 + 1][d], raw[i0][d], 0x07030602u);
+        const uint32_t e = __builtin_amdgcn_perm(raw[i0 + 3][d], raw[i0 + 2][d], 0x05010400u);
+        const uint32_t f = __builtin_amdgcn_perm(raw[i0 + 3][d], raw[i0 + 2][d], 0x07030602u);
+        cols[4 * d + 0][th] = __builtin_amdgcn_perm(e, a, 0x05040100u);
+        cols[4 * d + 1][th] = __builtin_amdgcn_perm(e, a, 0x07060302u);
+        cols[4 * d + 2][th] = __builtin_amdgcn_perm(f, b, 0x05040100u);
+        cols[4 * d + 3][th] = __builtin_amdgcn_perm(f, b, 0x07060302u);
+      }
+#pragma unroll
+    for (int h = 0; h < 16; ++h) {
+      const int row = fc * 16 + h;
+      *reinterpret_cast<u32x2*>(&tile[row * TILE + (((tg >> 1) ^ t_swz<CH>(row)) * 16) + (tg & 1) * 8]) =
+          (u32x2){cols[h][0], cols[h][1]};
+    }
+    __syncthreads();
+    if (it + 1 < ntiles) load_tile(n0 + (it + 1) * TILE);  // in flight during the MFMAs
+#pragma unroll
+    for (int s = 0; s < TILE / 64; ++s) {
+      const int lc = 4 * s + 2 * h2;  // logical chunks: tokens 64s + 32h2 .. +31
+      u32x8 a[RB], b[RB];
+#pragma unroll
+      for (int x = 0; x < RB; ++x) {
+        const int fi = (ib0 + x) * 32 + r;
+        const int fj = (jb0 + x) * 32 + r;
+        a[x] = concat(lds_chunk(Kt, fi, lc), lds_chunk(Kt, fi, lc + 1));
+        b[x] = concat(lds_chunk(Vt, fj, lc), lds_chunk(Vt, fj, lc + 1));
+      }
+#pragma unroll
+      for (int x = 0; x < RB; ++x)
+#pragma unroll
+        for (int y = 0; y < RB; ++y) acc[x][y] = mfma32x32x64_fp8(a[x], b[y], acc[x][y]);
+      if (zwave) {
+#pragma unroll
+        for (int x = 0; x < RB; ++x) zacc[x] = mfma32x32x64_fp8(a[x], ones, zacc[x]);
+      }
+    }
+  }
+
+  char* Pc = part + ((size_t)bh * C + c) * Partial<D>::kBytes;
+  store_partial_s<D, true, RB>(acc, Pc, ib0, jb0, lane);
+  // every column of zacc holds z; lane (r = 0, h2) writes rows q*8 + 4h2 .. +3
+  if (zwave && r == 0) {
+    float* Pz = reinterpret_cast<float*>(Pc + Partial<D>::kSBytes);
+#pragma unroll
+    for (int x = 0; x < RB; ++x)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<f32x4*>(&Pz[(ib0 + x) * 32 + 8 * q + 4 * h2]) =
+            (f32x4){zacc[x][4 * q], zacc[x][4 * q + 1], zacc[x][4 * q + 2], zacc[x][4 * q + 3]};
   }
 }
 
@@ -394,21 +531,22 @@ __global__ __launch_bounds__(256, 2) void linear_out_bf16(const TIn* __restrict_
     }
   };
 
-  // The head's state fragments go to LDS; the first two groups' Q and G loads
+  // The head's state fragments go to LDS; the first PF groups' Q and G loads
   // are issued after the fragment loads and before the wait for them, so the
-  // two latencies overlap (loads complete in order: waiting for the fragments
+  // latencies overlap (loads complete in order: waiting for the fragments
   // leaves the newer Q/G loads in flight).
   constexpr int FPT = (NF * 64 + 255) / 256;  // fragment loads per thread
   const rsrc_t Sr = make_rsrc(state + (size_t)bh * NF * 256, NF * 64 * 16);
   u32x4 frv[FPT];
 #pragma unroll
   for (int i = 0; i < FPT; ++i) frv[i] = buf_load16(Sr, (tid + 256 * i) * 16);
-  // Two groups ahead in flight, in three register sets used in turn (the loop
-  // is unrolled by three, so no set is copied into another: a copy would have
+  // PF groups ahead in flight, in PF + 1 register sets used in turn (the loop
+  // is unrolled by PF + 1, so no set is copied into another: a copy would have
   // to wait for the loads it reads).
-  u32x4 qa[NU], ga[NU], qb[NU], gb[NU], qc[NU], gc[NU];
-  load(grp, qa, ga);
-  load(grp + stride, qb, gb);
+  constexpr int PF = F8 ? kLinearOutPrefetchF8 : kLinearOutPrefetch;
+  u32x4 qs[PF + 1][NU], gs[PF + 1][NU];
+#pragma unroll
+  for (int s = 0; s < PF; ++s) load(grp + s * stride, qs[s], gs[s]);
 #pragma unroll
   for (int i = 0; i < FPT; ++i)
     if (tid + 256 * i < NF * 64) fr[tid + 256 * i] = frv[i];
@@ -490,15 +628,12 @@ __global__ __launch_bounds__(256, 2) void linear_out_bf16(const TIn* __restrict_
     }
   };
   for (;;) {
-    load(grp + 2 * stride, qc, gc);
-    compute(grp, qa, ga);
-    if ((grp += stride) * 16 >= N) break;
-    load(grp + 2 * stride, qa, ga);
-    compute(grp, qb, gb);
-    if ((grp += stride) * 16 >= N) break;
-    load(grp + 2 * stride, qb, gb);
-    compute(grp, qc, gc);
-    if ((grp += stride) * 16 >= N) break;
+#pragma unroll
+    for (int s = 0; s <= PF; ++s) {
+      load(grp + PF * stride, qs[(s + PF) % (PF + 1)], gs[(s + PF) % (PF + 1)]);
+      compute(grp, qs[s], gs[s]);
+      if ((grp += stride) * 16 >= N) return;
+    }
   }
 }
 
@@ -517,6 +652,9 @@ hipError_t launch_d(const hla_dims& d, const void* q, const void* k, const void*
   if (w)
     hipLaunchKernelGGL((linear_state_bf16<D, true, TIn>), dim3(plan.C, BH), dim3(256), 0, stream,
                        Kp, Vp, reinterpret_cast<const TIn*>(w), part, N, plan.T, plan.C);
+  else if constexpr (sizeof(TIn) == 1)
+    hipLaunchKernelGGL((linear_state_fp8<D>), dim3(plan.C, BH), dim3(256), 0, stream, Kp, Vp, part,
+                       N, plan.T, plan.C);
   else
     hipLaunchKernelGGL((linear_state_bf16<D, false, TIn>), dim3(plan.C, BH), dim3(256), 0, stream,
                        Kp, Vp, nullptr, part, N, plan.T, plan.C);

@@ -557,12 +557,20 @@ def test_linear_fp8_tails(N, D, out_dtype):
 
 
 @pytest.mark.parametrize("gated", [False, True])
-def test_linear_fp8_equals_bf16_path_on_same_values(gated):
-    # every e4m3 value is a bf16 value and the kernels convert exactly where
-    # they read, so the fp8 call differs from the bf16 call on the upcast
-    # tensors only by the order of the fp32 sums in phi(Q) S (the fp8 output
-    # pass takes the k-steps in another order); on these N(0,1) values every
-    # such sum is exact, so the two agree bit for bit
+def test_linear_fp8_matches_bf16_path_on_same_values(gated):
+    # every e4m3 value is a bf16 value and the kernels convert exactly, so the
+    # fp8 call computes what the bf16 call computes on the upcast tensors up to
+    # the order of fp32 sums: the fp8 output pass takes the k-steps of phi(Q) S
+    # in another order, and the plain fp8 state pass adds 64 products per matrix
+    # instruction where the bf16 one adds 16. The write-gated layer rounds
+    # beta * phi(K) to bf16 and runs the bf16 state pass, so only the output
+    # pass's order differs there; on these N(0,1) values those sums are exact
+    # and the two agree bit for bit. In the plain layer the fp8 instruction's own
+    # summation of its 64 products moves some fp32 partial states by more than
+    # an fp32 rounding, so a partial's bf16 rounding lands on the other side now
+    # and then: a few percent of the outputs move by about one bf16 step of
+    # their slab's largest value (measured: 2 % of them, 3.6e-3), and both calls
+    # stay equally close to the fp64 oracle
     q, k, v, g = make((2, 3, 1500, 128), 10100, FP8)
     w = wlogits((2, 3, 1500), 10200, FP8)
     up = [t.to(torch.bfloat16) for t in (q, k, v, g, w)]
@@ -571,16 +579,30 @@ def test_linear_fp8_equals_bf16_path_on_same_values(gated):
     else:
         a, b = run_linear(q, k, v, g), run_linear(*up[:4])
     assert a.dtype == b.dtype == torch.bfloat16
-    assert torch.equal(a, b)
+    if gated:
+        assert torch.equal(a, b)
+        return
+    a, b = a.float().cpu(), b.float().cpu()
+    ref = oracle.gated_linear(q, k, v, g, 1e-6)
+    differ = float((a != b).float().mean())
+    print(f"[fp8 vs bf16 path] differ {differ:.2e}, rel {rel_err(a, b):.2e}, "
+          f"oracle {rel_err(a, ref):.2e} / {rel_err(b, ref):.2e}", flush=True)
+    assert rel_err(a, ref) <= TOL[torch.bfloat16]
+    assert rel_err(b, ref) <= TOL[torch.bfloat16]
+    assert differ <= 0.05
+    assert rel_err(a, b) <= 2.0 ** -7
+    assert abs(rel_err(a, ref) - rel_err(b, ref)) <= 2.0 ** -8
 
 
 def test_linear_fp8_every_code_matches_bf16_path():
     # every finite e4m3 code (254 of them: zeros, subnormals, normals up to
     # +-448) in every input, so each conversion the kernels make meets every
-    # value. Magnitudes from 2^-9 to 448 make the fp32 sums of phi(Q) S round,
-    # and the fp8 output pass adds the k-steps in another order than the bf16
-    # one: outputs may then differ by one bf16 step, rarely; both stay within
-    # the tolerance of the fp64 oracle
+    # value. Magnitudes from 2^-9 to 448 make the fp32 sums round; the fp8
+    # state pass sums on the fp8 matrix instruction and the fp8 output pass
+    # adds the k-steps in another order than the bf16 one, so some outputs
+    # differ (measured: 5.7 % of them, by up to 5.2e-3 of their slab's largest
+    # value; relative to a cancelling near-zero output the step can be large).
+    # Both calls stay within the tolerance of the fp64 oracle
     codes = torch.tensor([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=torch.uint8)
     shape = (1, 2, 508, 128)
     gen = torch.Generator().manual_seed(10150)
@@ -598,8 +620,11 @@ def test_linear_fp8_every_code_matches_bf16_path():
     assert rel_err(a, ref) <= TOL[torch.bfloat16]
     assert rel_err(b, ref) <= TOL[torch.bfloat16]
     differ = (a != b)
-    assert int(differ.sum()) <= a.numel() // 1000
-    assert torch.all((a - b).abs() <= b.abs() * 2.0 ** -7)
+    print(f"[every e4m3 code] differ {int(differ.sum())} of {a.numel()}, "
+          f"max step {float(((a - b).abs() / b.abs().clamp_min(1e-30)).max()):.2e}, "
+          f"rel {rel_err(a, b):.2e}", flush=True)
+    assert int(differ.sum()) <= a.numel() // 10
+    assert rel_err(a, b) <= 2.0 ** -6
 
 
 def test_linear_fp8_binding_defaults_to_bf16_output():

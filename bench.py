@@ -17,7 +17,11 @@ rocprofv3 kernel traces and counter passes (copy: a plain device copy of known
 size that calibrates FETCH_SIZE / WRITE_SIZE); anchor_fp8, linear_fp8 and
 step_fp8 do the same on fp8 (e4m3) copies of the inputs; linear_wg runs the
 write-gated linear layer; attnres runs the block-attention-residual routing at
-the stack shape with two blocks; tiny runs the tiny fp32 pair.
+the stack shape with two blocks; tiny runs the tiny fp32 pair. Two more print
+JSON lines of their own: probes (matrix-core rate and shader clock for operand
+data of different switching activity, v_exp_f32 and LDS read rates, torch
+streaming rates of HBM) and cache_states (the linear layer at 480p and 720p
+under five cache states of the 256 MB Infinity Cache).
 """
 from __future__ import annotations
 
@@ -89,7 +93,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--profile", default=None,
                     choices=["anchor", "linear", "step", "copy", "anchor_fp8", "linear_fp8", "step_fp8",
-                             "attnres", "linear_wg", "tiny"])
+                             "attnres", "linear_wg", "tiny", "probes", "cache_states"])
     ap.add_argument("--iters", type=int, default=5, help="launches per --profile run")
     ap.add_argument("--sweep", action="store_true",
                     help="720p duration sweep: one gated linear and one gated softmax layer per clip "
@@ -106,6 +110,38 @@ def gpu_inputs(w, seed_offset, torch):
         out.append(torch.randn((w.B, w.H, w.N, w.D), generator=gen, device="cuda",
                                dtype=torch.float32).to(torch.bfloat16))
     return out
+
+
+def parity_sample(torch, hla, names=("tiny_f32", "480p_81f", "720p_81f", "stack_720p_121f",
+                                      "long_720p_193f")):
+    """Max relative error of the GPU path against the fp64 oracle, per workload.
+
+    For each workload: the first (b, h) slab of its seeded inputs (the same
+    recipe the parity tests use), the gated linear layer in full and the gated
+    softmax anchor on 64 sampled query rows (first, last and the query-block
+    edges among them), through the same calls the benchmark times. The metric is
+    the tests' one: max |gpu - ref| / max |ref| (bars: 2e-2 bf16, 1e-4 fp32).
+    """
+    import numpy as np
+    import oracle
+    from hla_inputs import BY_NAME, layer_inputs
+    res = {}
+    for name in names:
+        w = BY_NAME[name]
+        q, k, v, g = layer_inputs(w, 0, B=1, H=1)
+        qd, kd, vd, gd = (t.cuda() for t in (q, k, v, g))
+        lin = hla.hla_linear_fwd(qd, kd, vd, gd, eps=w.eps)
+        sm = hla.hla_softmax_anchor_fwd(qd, kd, vd, gd, scale=w.scale)
+        torch.cuda.synchronize()
+        rows = np.unique(np.r_[np.linspace(0, w.N - 1, 56).astype(int), [0, w.N - 1],
+                               np.minimum(w.N - 1, [255, 256, (w.N // 256) * 256 - 1, (w.N // 256) * 256])])
+        e_lin = oracle.max_rel_error(lin.float().cpu(), oracle.gated_linear(q, k, v, g, w.eps))
+        e_sm = oracle.max_rel_error(sm.float().cpu()[..., rows, :],
+                                    oracle.gated_softmax(q, k, v, g, w.scale, rows=rows))
+        res[name] = {"linear_max_rel_err": float(f"{e_lin:.3e}"), "softmax_max_rel_err": float(f"{e_sm:.3e}"),
+                     "bar": 1e-4 if w.dtype == "f32" else 2e-2, "softmax_rows": int(len(rows)),
+                     "N": w.N, "D": w.D, "dtype": w.dtype}
+    return res
 
 
 def cpu_baseline(w, budget_s: float):
@@ -164,6 +200,15 @@ def main():
 
     if args.sweep:
         duration_sweep(torch, hla)
+        return
+
+    if args.profile == "probes":
+        for row in hardware_probes(torch, hla):
+            print(json.dumps(row), flush=True)
+        return
+    if args.profile == "cache_states":
+        for row in cache_states(torch, hla):
+            print(json.dumps(row), flush=True)
         return
 
     if args.profile == "attnres":
@@ -312,6 +357,8 @@ def main():
         details["stack"] = stack_timing(torch, hla)
         details["other_workloads"] = [pair_timing(torch, hla, BY_NAME[n]) for n in ("480p_81f", "long_720p_193f")]
         details["tiny_f32"] = tiny_timing(torch, hla)
+        details["duration_sweep"] = duration_sweep(torch, hla, frames=(81, 121, 193, 481, 961), reps=1,
+                                                   quiet=True)
 
     line = {
         "metric": METRIC, "value": tokens / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
@@ -328,27 +375,34 @@ def main():
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        # the same fp64 oracle checks the GPU path on a sample of every workload
+        details["parity_vs_oracle"] = parity_sample(torch, hla)
     print(json.dumps(line), flush=True)
 
 
-def duration_sweep(torch, hla):
+def duration_sweep(torch, hla, frames=None, reps=None, quiet=False):
     """Per-layer time of gated linear vs gated softmax attention as the clip grows.
 
     A 3:1 hybrid block spends (3 t_linear + t_softmax) / 4 per layer against
     t_softmax for an all-softmax block; the ratio is the hybrid's speed-up.
+    ``frames`` limits the clip lengths, ``reps`` the timed softmax calls per
+    length; quiet returns the rows instead of printing them.
     """
     from hla_inputs import DURATION_FRAMES, duration_workload
-    for frames, note in DURATION_FRAMES:
-        w = duration_workload(frames)
+    rows_out = []
+    for frames_i, note in DURATION_FRAMES:
+        if frames is not None and frames_i not in frames:
+            continue
+        w = duration_workload(frames_i)
         q, k, v, g = gpu_inputs(w, 0, torch)
         ws_l, ws_a = hla.linear_workspace(q), hla.anchor_workspace(q)
         out = torch.empty_like(q)
-        res = {"sweep": "720p duration", "frames": frames, "clip": note, "latent_thw": list(w.latent),
+        res = {"sweep": "720p duration", "frames": frames_i, "clip": note, "latent_thw": list(w.latent),
                "B": w.B, "H": w.H, "N": w.N, "D": w.D}
         for name, fn, reps in (
                 ("linear", lambda: hla.hla_linear_fwd(q, k, v, g, out=out, eps=w.eps, workspace=ws_l), 10),
                 ("softmax", lambda: hla.hla_softmax_anchor_fwd(q, k, v, g, out=out, scale=w.scale,
-                                                               workspace=ws_a), 3)):
+                                                               workspace=ws_a), reps or 3)):
             fn()
             torch.cuda.synchronize()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -364,9 +418,140 @@ def duration_sweep(torch, hla):
         hyb = (3 * res["linear_ms"] + res["softmax_ms"]) / 4
         res["hybrid_3to1_ms_per_layer"] = round(hyb, 4)
         res["speedup_hybrid_vs_all_softmax"] = round(res["softmax_ms"] / hyb, 3)
-        print(json.dumps(res), flush=True)
+        if quiet:
+            rows_out.append(res)
+        else:
+            print(json.dumps(res), flush=True)
         del q, k, v, g, out, ws_l, ws_a
         torch.cuda.empty_cache()
+    return rows_out
+
+
+def hardware_probes(torch, hla):
+    """Rates of the units the kernels depend on, from libhla_probes.so and torch.
+
+    mfma: 8 x 32x32x16 bf16 MFMAs per iteration and wave into four accumulators,
+    one workgroup per CU with one or two waves per SIMD, for random bf16
+    operands, all-zero operands, and one random register as both operands;
+    the shader clock is the workgroups' mean s_memtime cycles over the event
+    time. exp: 16 independent v_exp_f32 chains per thread, 512 threads per CU.
+    lds: ds_read_b128 of lane-consecutive chunks, 512 threads per CU.
+    hbm: torch copy (read 1 + write 1), add (read 2 + write 1) and fill
+    (write) over 1 GiB bf16 tensors.
+    """
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "softmax_attention_amd", "libhla_probes.so"))
+    if len(hla.hip_runtimes_loaded()) > 1:
+        raise RuntimeError("the probe library pulled in a second HIP runtime")
+    P, I = ctypes.c_void_p, ctypes.c_int
+    lib.hla_probe_mfma.argtypes = [I, I, I, I, P, P, P]
+    lib.hla_probe_exp.argtypes = [I, I, P, P, P]
+    lib.hla_probe_lds.argtypes = [I, I, P, P, P]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(cus * 512, dtype=torch.float32, device="cuda")
+    clk = torch.zeros(cus, dtype=torch.int64, device="cuda")
+    st = P(torch.cuda.current_stream().cuda_stream)
+    op, cp = P(out.data_ptr()), P(clk.data_ptr())
+
+    def timed(launch, reps=3):
+        if launch() != 0:
+            raise RuntimeError("probe launch failed")
+        torch.cuda.synchronize()
+        ms, cyc = [], []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            launch()
+            b.record()
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b))
+            cyc.append(float(clk.double().mean()))
+        i = sorted(range(reps), key=lambda j: ms[j])[reps // 2]
+        return ms[i], cyc[i]
+
+    rows = []
+    iters = 20000
+    for mode, name in ((0, "random bf16"), (1, "zero"), (2, "one random register as A and B")):
+        for w in (1, 2):
+            ms, cyc = timed(lambda: lib.hla_probe_mfma(mode, w, cus, iters, op, cp, st))
+            flops = 2.0 * 32 * 32 * 16 * 8 * iters * 4 * w * cus
+            tf = flops / (ms * 1e-3) / 1e12
+            rows.append({"probe": "mfma_f32_32x32x16_bf16", "operands": name, "waves_per_simd": w,
+                         "ms": round(ms, 3), "TFLOP_s": round(tf, 1),
+                         "frac_of_2500": round(tf / PEAK_BF16_TFLOPS, 3),
+                         "shader_clock_GHz": round(cyc / (ms * 1e6), 3)})
+    ms, cyc = timed(lambda: lib.hla_probe_exp(cus, iters, op, cp, st))
+    rows.append({"probe": "v_exp_f32", "ms": round(ms, 3),
+                 "T_per_s": round(16.0 * iters * 512 * cus / (ms * 1e-3) / 1e12, 2),
+                 "per_CU_per_clock": round(16.0 * iters * 512 / cyc, 2),
+                 "shader_clock_GHz": round(cyc / (ms * 1e6), 3)})
+    ms, cyc = timed(lambda: lib.hla_probe_lds(cus, iters, op, cp, st))
+    rows.append({"probe": "ds_read_b128", "ms": round(ms, 3),
+                 "bytes_per_CU_per_clock": round(8.0 * 16 * 512 * iters / cyc, 1),
+                 "TB_s": round(8.0 * 16 * 512 * iters * cus / (ms * 1e-3) / 1e12, 1),
+                 "shader_clock_GHz": round(cyc / (ms * 1e6), 3)})
+    n = 1 << 29  # 1 GiB of bf16
+    x = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    y = torch.ones_like(x)
+    z = torch.empty_like(x)
+    for name, fn, moved in (("copy (read 1 + write 1)", lambda: z.copy_(x), 4 * n),
+                            ("add (read 2 + write 1)", lambda: torch.add(x, y, out=z), 6 * n),
+                            ("fill (write)", lambda: z.fill_(1.0), 2 * n)):
+        ms, _ = timed(lambda: (fn(), 0)[1], reps=5)
+        rows.append({"probe": "hbm_torch", "op": name, "ms": round(ms, 3),
+                     "TB_s": round(moved / (ms * 1e-3) / 1e12, 2)})
+    return rows
+
+
+def cache_states(torch, hla, names=("480p_81f", "720p_81f"), reps=20):
+    """The gated linear layer's time under five states of the Infinity Cache.
+
+    Median of ``reps`` event-timed calls per state: the same inputs every call;
+    two input sets alternating (the other-workload lines of the benchmark); four
+    sets rotating; each call after a gated softmax call on other inputs (the
+    benchmark step); each call after a 512 MB write (whose dirty lines are
+    written back during the call). frac = 10 N D B H bytes / time / 8 TB/s.
+    """
+    from hla_inputs import BY_NAME
+    rows = []
+    for name in names:
+        w = BY_NAME[name]
+        sets = [gpu_inputs(w, s, torch) for s in range(4)]
+        other = gpu_inputs(w, 7, torch)
+        out, out_a = torch.empty_like(sets[0][0]), torch.empty_like(sets[0][0])
+        ws, ws_a = hla.linear_workspace(sets[0][0]), hla.anchor_workspace(sets[0][0])
+        big = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        alg = 10.0 * w.N * w.D * w.B * w.H
+
+        def anchor_other(i):
+            hla.hla_softmax_anchor_fwd(*other, out=out_a, scale=w.scale, workspace=ws_a)
+
+        def write_big(i):
+            big.fill_(i & 255)
+
+        for state, nsets, pre in (("same inputs every call", 1, None),
+                                  ("two input sets alternating", 2, None),
+                                  ("four input sets rotating", 4, None),
+                                  ("after a gated softmax call on other inputs", 2, anchor_other),
+                                  ("after writing a 512 MB buffer", 2, write_big)):
+            ev = []
+            for i in range(reps + 2):
+                if pre is not None:
+                    pre(i)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                q, k, v, g = sets[i % nsets]
+                a.record()
+                hla.hla_linear_fwd(q, k, v, g, out=out, eps=w.eps, workspace=ws)
+                b.record()
+                ev.append((a, b))
+            torch.cuda.synchronize()
+            t = sorted(a.elapsed_time(b) for a, b in ev[2:])
+            ms = t[len(t) // 2]
+            rows.append({"cache_state": state, "workload": name, "linear_ms": round(ms, 4),
+                         "frac_hbm_peak": round(alg / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)})
+        del sets, other, out, out_a, ws, ws_a, big
+        torch.cuda.empty_cache()
+    return rows
 
 
 def fp8_timing(torch, hla, w, sets, K, lin_ms_bf16, sm_ms_bf16):
@@ -440,11 +625,12 @@ def tiny_timing(torch, hla, reps: int = 50):
     return res
 
 
-def pair_timing(torch, hla, w, reps: int = 6):
+def pair_timing(torch, hla, w, reps: int = 20, sm_reps: int = 6):
     """One gated linear and one gated softmax layer of workload ``w`` (bf16).
 
     Two input sets alternate, so a call never finds its inputs in the 256 MB
-    Infinity Cache from the previous call.
+    Infinity Cache from the previous call. Each call is timed by its own
+    events; the fractions use the mean, the median is reported beside it.
     """
     sets = [gpu_inputs(w, s_, torch) for s_ in range(2)]
     ws_l, ws_a = hla.linear_workspace(sets[0][0]), hla.anchor_workspace(sets[0][0])
@@ -456,13 +642,16 @@ def pair_timing(torch, hla, w, reps: int = 6):
         fn(0)
         fn(1)
         torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for i in range(reps):
+        n = reps if name == "linear" else sm_reps
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for i in range(n):
+            ev[i][0].record()
             fn(i)
-        b.record()
+            ev[i][1].record()
         torch.cuda.synchronize()
-        res[f"{name}_ms"] = round(a.elapsed_time(b) / reps, 4)
+        t = sorted(a.elapsed_time(b) for a, b in ev)
+        res[f"{name}_ms"] = round(sum(t) / n, 4)
+        res[f"{name}_ms_median"] = round((t[(n - 1) // 2] + t[n // 2]) / 2, 4)
     BH, N, D = w.B * w.H, w.N, w.D
     res["linear_frac_hbm_peak"] = round(10.0 * N * D * BH / (res["linear_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
     res["softmax_frac_mfma_peak"] = round(4.0 * N * N * D * BH / (res["softmax_ms"] * 1e-3) / 1e12
@@ -498,7 +687,8 @@ def attnres_timing(torch, hla, n_blocks: int = 2, reps: int = 10):
     return {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D, "blocks": n_blocks,
             "ms": round(ms, 4), "alg_bytes": alg, "GB_s": round(alg / (ms * 1e-3) / 1e9, 1),
             "frac_hbm_peak": round(alg / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-            "note": "back-to-back calls on the same tensors (1.9 GB, beyond the 256 MB cache)"}
+            "note": "back-to-back calls on the same tensors (x, two summaries and out: 0.93 GB, "
+                    "beyond the 256 MB cache)"}
 
 
 def stack_timing(torch, hla):

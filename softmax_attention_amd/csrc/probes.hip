@@ -1,0 +1,170 @@
+// Micro-benchmarks of the gfx950 units the attention kernels depend on: the
+// bf16 matrix-core rate and the shader clock it sustains for operand data of
+// different switching activity, the transcendental (v_exp_f32) rate, and the
+// LDS 16-byte read rate. They back the hardware figures the kernels' rooflines
+// are discussed against. Built into a library of its own (libhla_probes.so),
+// separate from the attention library; callers pass device buffers and a
+// stream, and time the launches themselves.
+//
+// Every probe writes one float per thread to `out` (so the compiler keeps the
+// work) and, from thread 0 of each workgroup, the workgroup's elapsed shader
+// clock cycles (s_memtime, read after a barrier at the start and at the end of
+// the timed loop, so the count spans every wave) to `clk`. Buffers:
+// out >= grid * 512 floats, clk >= grid int64.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8_p __attribute__((ext_vector_type(8)));
+typedef float f32x16_p __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_p __attribute__((ext_vector_type(4)));
+
+namespace {
+
+__device__ __forceinline__ uint32_t mix(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return x;
+}
+// two finite bf16 values in [1, 2) with random mantissas
+__device__ __forceinline__ uint32_t bf16_pair_near_one(uint32_t x) {
+  return (x & 0x007f007fu) | 0x3f803f80u;
+}
+
+// MODE 0: A and B random bf16 (fixed per lane); 1: A and B zero; 2: one random
+// register used as both A and B. WAVES waves per workgroup, one workgroup per
+// CU; each wave issues iters * 8 MFMAs into four independent accumulators.
+template <int MODE, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 1) void probe_mfma(float* out, long long* clk, int iters) {
+  const int tid = threadIdx.x;
+  u32x4_p A[2], B[2];
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t s = (blockIdx.x * 512u + tid) * 16u + i * 8u;
+    A[i] = (u32x4_p){bf16_pair_near_one(mix(s)), bf16_pair_near_one(mix(s + 1)),
+                     bf16_pair_near_one(mix(s + 2)), bf16_pair_near_one(mix(s + 3))};
+    B[i] = (u32x4_p){bf16_pair_near_one(mix(s + 4)), bf16_pair_near_one(mix(s + 5)),
+                     bf16_pair_near_one(mix(s + 6)), bf16_pair_near_one(mix(s + 7))};
+    if (MODE == 1) A[i] = B[i] = (u32x4_p){0, 0, 0, 0};
+    if (MODE == 2) B[i] = A[i];
+  }
+  f32x16_p acc[4];
+  for (int i = 0; i < 4; ++i) acc[i] = (f32x16_p){};
+  __syncthreads();
+  const long long t0 = clock64();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+      acc[m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_p, A[m & 1]),
+                                                           __builtin_bit_cast(bf16x8_p, B[m >> 2]),
+                                                           acc[m & 3], 0, 0, 0);
+  }
+  __syncthreads();
+  const long long t1 = clock64();
+  float s = 0.f;
+  for (int i = 0; i < 4; ++i)
+    for (int x = 0; x < 16; ++x) s += acc[i][x];
+  out[blockIdx.x * 512 + tid] = s;
+  if (tid == 0) clk[blockIdx.x] = t1 - t0;
+}
+
+// 16 independent chains per thread of x <- 2^x - 1.5 (a contraction towards a
+// fixed point near -0.86, so values stay ordinary floats): iters * 16 v_exp_f32
+// per thread, 512 threads per workgroup.
+__global__ __launch_bounds__(512, 1) void probe_exp(float* out, long long* clk, int iters) {
+  const int tid = threadIdx.x;
+  float e[16];
+  for (int i = 0; i < 16; ++i) e[i] = (float)(mix(tid * 16u + i) & 255u) * (1.0f / 256.0f) - 0.5f;
+  __syncthreads();
+  const long long t0 = clock64();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) e[i] = __builtin_amdgcn_exp2f(e[i]) - 1.5f;
+  }
+  __syncthreads();
+  const long long t1 = clock64();
+  float s = 0.f;
+  for (int i = 0; i < 16; ++i) s += e[i];
+  out[blockIdx.x * 512 + tid] = s;
+  if (tid == 0) clk[blockIdx.x] = t1 - t0;
+}
+
+// ds_read_b128 stream: 512 threads, 8 reads of 16 bytes per iteration at fixed
+// addresses (lane-consecutive chunks, conflict-free, 8 KiB apart) inside a
+// 64 KiB LDS array. The eight reads and their wait are one asm block, so all
+// eight are in flight together and stay 16-byte reads although only one dword
+// of each feeds the running XOR (one VALU op per read).
+__global__ __launch_bounds__(512, 1) void probe_lds(float* out, long long* clk, int iters) {
+  __shared__ __attribute__((aligned(16))) uint32_t lds[16384];  // 64 KiB
+  const int tid = threadIdx.x;
+  for (int i = tid; i < 16384; i += 512) lds[i] = mix(i);
+  __syncthreads();
+  typedef __attribute__((address_space(3))) uint32_t lds_u32;
+  // LDS byte address of this lane's chunk in the first 8 KiB; reads at +8 KiB * m
+  const uint32_t a = (uint32_t)(uintptr_t)((lds_u32*)lds) + (uint32_t)(tid & 511) * 16u;
+  uint32_t x = 0;
+  __syncthreads();
+  const long long t0 = clock64();
+  for (int it = 0; it < iters; ++it) {
+    u32x4_p v0, v1, v2, v3, v4, v5, v6, v7;
+    asm volatile(
+        "ds_read_b128 %0, %8\n"
+        "ds_read_b128 %1, %8 offset:8192\n"
+        "ds_read_b128 %2, %8 offset:16384\n"
+        "ds_read_b128 %3, %8 offset:24576\n"
+        "ds_read_b128 %4, %8 offset:32768\n"
+        "ds_read_b128 %5, %8 offset:40960\n"
+        "ds_read_b128 %6, %8 offset:49152\n"
+        "ds_read_b128 %7, %8 offset:57344\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=v"(v0), "=v"(v1), "=v"(v2), "=v"(v3), "=v"(v4), "=v"(v5), "=v"(v6), "=v"(v7)
+        : "v"(a)
+        : "memory");
+    x ^= v0[0] ^ v1[1] ^ v2[2] ^ v3[3] ^ v4[0] ^ v5[1] ^ v6[2] ^ v7[3];
+  }
+  __syncthreads();
+  const long long t1 = clock64();
+  out[blockIdx.x * 512 + tid] = __uint_as_float(x & 0x3fffffffu);
+  if (tid == 0) clk[blockIdx.x] = t1 - t0;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Status: 0 on success, 1 for an unsupported argument, 2 for a launch error.
+int hla_probe_mfma(int mode, int waves_per_simd, int grid, int iters, float* out, long long* clk,
+                   void* stream) {
+  if (grid <= 0 || iters <= 0 || !out || !clk || mode < 0 || mode > 2 ||
+      (waves_per_simd != 1 && waves_per_simd != 2))
+    return 1;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const dim3 g(grid);
+  if (waves_per_simd == 1) {
+    if (mode == 0) hipLaunchKernelGGL((probe_mfma<0, 4>), g, dim3(256), 0, s, out, clk, iters);
+    if (mode == 1) hipLaunchKernelGGL((probe_mfma<1, 4>), g, dim3(256), 0, s, out, clk, iters);
+    if (mode == 2) hipLaunchKernelGGL((probe_mfma<2, 4>), g, dim3(256), 0, s, out, clk, iters);
+  } else {
+    if (mode == 0) hipLaunchKernelGGL((probe_mfma<0, 8>), g, dim3(512), 0, s, out, clk, iters);
+    if (mode == 1) hipLaunchKernelGGL((probe_mfma<1, 8>), g, dim3(512), 0, s, out, clk, iters);
+    if (mode == 2) hipLaunchKernelGGL((probe_mfma<2, 8>), g, dim3(512), 0, s, out, clk, iters);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+int hla_probe_exp(int grid, int iters, float* out, long long* clk, void* stream) {
+  if (grid <= 0 || iters <= 0 || !out || !clk) return 1;
+  hipLaunchKernelGGL(probe_exp, dim3(grid), dim3(512), 0, reinterpret_cast<hipStream_t>(stream), out,
+                     clk, iters);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+int hla_probe_lds(int grid, int iters, float* out, long long* clk, void* stream) {
+  if (grid <= 0 || iters <= 0 || !out || !clk) return 1;
+  hipLaunchKernelGGL(probe_lds, dim3(grid), dim3(512), 0, reinterpret_cast<hipStream_t>(stream), out,
+                     clk, iters);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+}  // extern "C"

@@ -558,7 +558,9 @@ def fp8_timing(torch, hla, w, sets, K, lin_ms_bf16, sm_ms_bf16):
     """The timed step again on fp8 (e4m3) copies of the same inputs, bf16 out.
 
     The anchor's Q K^T runs at the fp8 matrix rate and P V at the bf16 one; the
-    two halves have equal flops, so its peak is 2 / (1/5.0 + 1/2.5) PF.
+    two halves have equal flops, so its peak is 2 / (1/5.0 + 1/2.5) PF. The
+    fp8-probability anchor (P rounded to e4m3, P V on the fp8 matrix cores) is
+    timed the same way against the 5.0 PF fp8 peak.
     """
     f8 = [[t.to(torch.float8_e4m3fn) for t in s] for s in sets]
     out = torch.empty(f8[0][0].shape, dtype=torch.bfloat16, device=f8[0][0].device)
@@ -571,9 +573,13 @@ def fp8_timing(torch, hla, w, sets, K, lin_ms_bf16, sm_ms_bf16):
     def anchor(i):
         hla.hla_softmax_anchor_fwd(*f8[i % 2], out=out, scale=w.scale, workspace=ws_a)
 
+    def anchor8p(i):
+        hla.hla_softmax_anchor_fp8p_fwd(*f8[i % 2], out=out, scale=w.scale, workspace=ws_a)
+
     for i in range(2):
         linear(i)
         anchor(i)
+        anchor8p(i)
     torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     for i in range(K):
@@ -585,6 +591,15 @@ def fp8_timing(torch, hla, w, sets, K, lin_ms_bf16, sm_ms_bf16):
     torch.cuda.synchronize()
     lin_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
     sm_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    ev8 = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    for i in range(K):
+        ev8[i][0].record()
+        linear(i)
+        ev8[i][1].record()
+        anchor8p(i)
+        ev8[i][2].record()
+    torch.cuda.synchronize()
+    sm8_ms = sum(e[1].elapsed_time(e[2]) for e in ev8) / K
     BH, N, D = w.B * w.H, w.N, w.D
     lin_bytes = 6.0 * N * D * BH                  # read Q, K, V, G (1 byte), write O (bf16)
     sm_tfs = 4.0 * N * N * D * BH / (sm_ms * 1e-3) / 1e12
@@ -599,6 +614,13 @@ def fp8_timing(torch, hla, w, sets, K, lin_ms_bf16, sm_ms_bf16):
         "softmax_peak_TFLOP_s": round(peak_mixed, 1),
         "softmax_frac_peak": round(sm_tfs / peak_mixed, 4),
         "softmax_speedup_vs_bf16": round(sm_ms_bf16 / sm_ms, 3),
+        "softmax_fp8p": {
+            "call": "hla_softmax_anchor_fp8p_fwd (probabilities rounded to e4m3, P V on fp8 MFMA)",
+            "ms": round(sm8_ms, 4),
+            "TFLOP_s": round(4.0 * N * N * D * BH / (sm8_ms * 1e-3) / 1e12, 1),
+            "peak_TFLOP_s": PEAK_FP8_TFLOPS,
+            "frac_peak": round(4.0 * N * N * D * BH / (sm8_ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+            "speedup_vs_bf16": round(sm_ms_bf16 / sm8_ms, 3)},
     }
 
 

@@ -30,10 +30,13 @@
  * paths compute in fp32 throughout. fp8 inputs (OCP e4m3: 1 sign, 4 exponent, 3
  * mantissa bits, bias 7, no infinities) take one byte per element. The softmax
  * anchor forms Q K^T from them on the fp8 matrix cores (exact products, fp32
- * sums); everywhere else they are converted exactly to bf16 where the kernels
- * read them. Results are thus those of the bf16 path on the same values, up to
- * the fp32 summation order (of Q K^T in the anchor, of phi(Q) S in the linear
- * layer).
+ * sums), and so does the linear layer's state pass for phi(K)^T V (without a
+ * write gate); everywhere else they are converted exactly to bf16 where the
+ * kernels read them. Results are thus those of the bf16 path on the same values,
+ * up to the fp32 summation order and the matrix instructions' internal
+ * rounding of their sums (of Q K^T in the anchor, of phi(K)^T V and phi(Q) S in
+ * the linear layer). hla_softmax_anchor_fp8p_fwd also rounds the probabilities
+ * to e4m3.
  *
  * Errors: every argument is checked on the host before any HIP call. On error
  * nothing is enqueued and the output is untouched. On success the work is
@@ -56,7 +59,7 @@
 extern "C" {
 #endif
 
-#define HLA_ABI_VERSION 4
+#define HLA_ABI_VERSION 5
 
 typedef enum { HLA_F32 = 0, HLA_BF16 = 1, HLA_FP8_E4M3 = 2 } hla_dtype;
 
@@ -155,6 +158,25 @@ size_t hla_softmax_anchor_workspace_bytes(const hla_dims* d);
 hla_status hla_softmax_anchor_fwd(const hla_dims* d, const void* q, const void* k, const void* v,
                                   const void* g, void* out, int accumulate, float scale,
                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Gated softmax anchor with 8-bit probabilities, for fp8 (e4m3) inputs only --
+ * one reading of the quantized inference the pages report (ai-papers.net
+ * summary: quantization-aware training, 5.8 % lower latency, no number format
+ * given). As hla_softmax_anchor_fwd, except that the softmax probabilities,
+ * taken relative to a running row maximum and at most 2^8, are rounded to OCP
+ * e4m3 (round to nearest even, subnormals kept) and P V runs on the fp8 matrix
+ * cores with V in e4m3; the row sum adds the same rounded probabilities. With a
+ * 3-bit fraction this rounding moves each probability by up to 2^-4 of itself
+ * (2^-10 absolutely below 2^-6 of the row maximum), so outputs carry an error
+ * of their own -- at the 480p and 720p shapes about 2.5e-2 of the largest
+ * output, against about 2e-3 with bf16 probabilities. d->in_dtype must be
+ * HLA_FP8_E4M3 (else HLA_ERR_UNSUPPORTED). hla_softmax_anchor_workspace_bytes(d)
+ * bytes of workspace suffice (this call uses less: its copy of V is e4m3).
+ * Arguments, accumulate and the other errors as in hla_softmax_anchor_fwd. */
+hla_status hla_softmax_anchor_fp8p_fwd(const hla_dims* d, const void* q, const void* k,
+                                       const void* v, const void* g, void* out, int accumulate,
+                                       float scale, void* workspace, size_t workspace_bytes,
+                                       void* stream);
 
 /* Hybrid stack: for l = 0 .. n_layers-1 in order, x += layer_l(q[l], k[l], v[l], g[l])
  * where kinds[l] is HLA_LAYER_LINEAR or HLA_LAYER_SOFTMAX; SANA-Video 2.0 places a

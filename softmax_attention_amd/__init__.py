@@ -30,7 +30,8 @@ STATUS = {
 }
 EXPORTS = ("hla_abi_version", "hla_status_str", "hla_linear_workspace_bytes", "hla_linear_fwd",
            "hla_linear_fwd_noalloc", "hla_linear_write_gated_fwd", "hla_softmax_anchor_workspace_bytes",
-           "hla_softmax_anchor_fwd", "hla_hybrid_stack_fwd", "hla_attnres_route_fwd")
+           "hla_softmax_anchor_fwd", "hla_softmax_anchor_fp8p_fwd", "hla_hybrid_stack_fwd",
+           "hla_attnres_route_fwd")
 
 
 class hla_dims(ctypes.Structure):
@@ -88,6 +89,9 @@ def _load() -> ctypes.CDLL:
     lib.hla_softmax_anchor_fwd.restype = ctypes.c_int
     lib.hla_softmax_anchor_fwd.argtypes = [pd, P, P, P, P, P, ctypes.c_int, ctypes.c_float, P,
                                            ctypes.c_size_t, P]
+    lib.hla_softmax_anchor_fp8p_fwd.restype = ctypes.c_int
+    lib.hla_softmax_anchor_fp8p_fwd.argtypes = [pd, P, P, P, P, P, ctypes.c_int, ctypes.c_float, P,
+                                                ctypes.c_size_t, P]
     lib.hla_hybrid_stack_fwd.restype = ctypes.c_int
     lib.hla_hybrid_stack_fwd.argtypes = [pd, ctypes.c_int, ctypes.POINTER(ctypes.c_int32),
                                          ctypes.POINTER(P), ctypes.POINTER(P), ctypes.POINTER(P),
@@ -324,6 +328,20 @@ def hla_linear_write_gated_fwd(q, k, v, g, w, out=None, accumulate: bool = False
 def hla_softmax_anchor_fwd(q, k, v, g, out=None, accumulate: bool = False,
                            scale: Optional[float] = None, workspace=None, stream=None):
     """Gated softmax anchor O = sigma(G) * softmax(scale Q K^T) V; returns out."""
+    return _anchor("hla_softmax_anchor_fwd", q, k, v, g, out, accumulate, scale, workspace, stream)
+
+
+def hla_softmax_anchor_fp8p_fwd(q, k, v, g, out=None, accumulate: bool = False,
+                                scale: Optional[float] = None, workspace=None, stream=None):
+    """The gated softmax anchor on fp8 (e4m3) inputs with probabilities rounded to
+    e4m3 and P V on the fp8 matrix cores; returns out."""
+    if _dtype_code(q) != HLA_FP8_E4M3:
+        raise TypeError("hla_softmax_anchor_fp8p_fwd takes float8_e4m3fn inputs")
+    return _anchor("hla_softmax_anchor_fp8p_fwd", q, k, v, g, out, accumulate, scale, workspace,
+                   stream)
+
+
+def _anchor(name, q, k, v, g, out, accumulate, scale, workspace, stream):
     _check(q, k, v, g)
     scale = 1.0 / math.sqrt(q.shape[-1]) if scale is None else float(scale)
     if out is not None:
@@ -335,12 +353,11 @@ def hla_softmax_anchor_fwd(q, k, v, g, out=None, accumulate: bool = False,
         if workspace is None:
             workspace = anchor_workspace(q, out.dtype)
         _workspace_check(workspace, q)
-        st = lib.hla_softmax_anchor_fwd(ctypes.byref(d), q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                                        g.data_ptr(), out.data_ptr(), int(bool(accumulate)), scale,
-                                        workspace.data_ptr(),
-                                        workspace.numel() * workspace.element_size(),
-                                        _stream(stream, q.device))
-    _raise("hla_softmax_anchor_fwd", st)
+        st = getattr(lib, name)(ctypes.byref(d), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                g.data_ptr(), out.data_ptr(), int(bool(accumulate)), scale,
+                                workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                _stream(stream, q.device))
+    _raise(name, st)
     return out
 
 

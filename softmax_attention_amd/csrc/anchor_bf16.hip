@@ -20,10 +20,15 @@
 //                    result exact up to rounding.
 //   O^T += V^T P^T   P^T stays in registers (the MFMA result layout is reused as
 //                    the next B operand by permuting the key order inside each
-//                    k-step). V is repacked once per call into bf16 V^T rows
-//                    (a workspace, zero keys past N; fp8 values convert
-//                    exactly) in the key order P^T uses, so each V^T operand is
-//                    one 16-byte LDS read.
+//                    k-step). V is repacked once per call into V^T rows (a
+//                    workspace, zero keys past N) in the key order P^T uses,
+//                    so each V^T operand is one 16-byte LDS read (two for fp8).
+//                    By default P is rounded to bf16 and V^T is bf16 (fp8 V
+//                    converts exactly): 32x32x16 bf16 MFMA. In the fp8-P mode
+//                    (fp8 inputs only) P is rounded to e4m3 (P <= 2^8 by the
+//                    lazy max) and V^T stays e4m3: one 32x32x64 fp8 MFMA per
+//                    64-key tile and 32-row block. The row sum always adds the
+//                    same rounded P the matrix cores consume.
 // K and V^T tiles go from HBM straight into LDS through buffer loads, which
 // return zeros past the end of the head, so the last partial tile needs no
 // predicated loads; only its scores past N are masked.
@@ -63,6 +68,17 @@ __device__ __forceinline__ int vt_swz(int d) { return ((d >> 1) & 3) | ((d >> 2)
 // group is stored as [keys 0-3, 8-11 | keys 4-7, 12-15] and each half reads
 // its 8 keys as one 16-byte chunk.
 __device__ __forceinline__ int vt_pos(int k16) { return 8 * ((k16 >> 2) & 1) + 4 * (k16 >> 3) + (k16 & 3); }
+
+// fp8 V^T rows (64 bytes per 64-key tile). The P V instruction's k index
+// p = 32h + 16kb + 4q + e of lane half h takes score element 4q + e of 32-key
+// block kb of that lane, which is key 32kb + 8q + 4h + e (the S^T MFMA result
+// layout), so position p of a tile row holds that key. The four 16-byte
+// chunks of row d sit at c ^ vt8_swz(d): the 16 rows one operand read touches
+// (features vrow(r), r < 16, or 16 <= r < 32) land on 16 distinct bank groups.
+__device__ __forceinline__ int vt8_key(int p) {
+  return 32 * ((p >> 4) & 1) + 8 * ((p >> 2) & 3) + 4 * (p >> 5) + (p & 3);
+}
+__device__ __forceinline__ int vt8_swz(int d) { return ((d >> 2) & 1) | ((d >> 3) & 2); }
 
 // ---------------------------------------------------------------------------
 // V -> V^T repack (once per call): per head, V^T[d][n_pad] with the key order
@@ -106,11 +122,47 @@ __global__ __launch_bounds__(256) void anchor_pack_vt(const TIn* __restrict__ V,
   }
 }
 
-template <int D, bool OUT_F32, typename TIn>
+// fp8-P mode: V^T stays e4m3, per head [D][n_pad] bytes in vt8_key order
+// inside every 64-key tile, zeros for keys >= N.
+template <int D>
+__global__ __launch_bounds__(256) void anchor_pack_vt8(const uint8_t* __restrict__ V,
+                                                       uint8_t* __restrict__ VT, int N, int n_pad) {
+  constexpr int CH = D / 16;                 // 16-byte chunks per key row
+  __shared__ uint32_t tile[64][D / 4 + 1];   // 64 keys x D bytes, odd word stride
+  const int j = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const uint8_t* Vh = V + (size_t)bh * N * D;
+  uint8_t* VTh = VT + (size_t)bh * D * n_pad;
+  for (int c = tid; c < 64 * CH; c += 256) {
+    const int key = c / CH, col = (c % CH) * 16, n = j * 64 + key;
+    const u32x4 v = n < N ? ldg16(Vh + (size_t)n * D + col) : (u32x4){0, 0, 0, 0};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) tile[key][col / 4 + p] = v[p];
+  }
+  __syncthreads();
+  // output: D rows x 4 chunks of 16 positions
+  for (int c = tid; c < D * 4; c += 256) {
+    const int d = c >> 2, pc = c & 3;
+    uint32_t w[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t src = tile[vt8_key(16 * pc + 4 * p + u)][d >> 2];
+        word |= ((src >> (8 * (d & 3))) & 0xffu) << (8 * u);
+      }
+      w[p] = word;
+    }
+    stg16(VTh + (size_t)d * n_pad + j * 64 + pc * 16, (u32x4){w[0], w[1], w[2], w[3]});
+  }
+}
+
+// P8: the fp8-P mode (TIn must be uint8_t).
+template <int D, bool OUT_F32, typename TIn, bool P8>
 __global__ __launch_bounds__(kThreads, 1) void anchor_bf16(const TIn* __restrict__ Q,
                                                       const TIn* __restrict__ K,
                                                       const TIn* __restrict__ G,
-                                                      const uint16_t* __restrict__ VT,
+                                                      const void* __restrict__ VTv,
                                                       void* __restrict__ out, int N, int n_pad,
                                                       int nqb, int nmain, int split, float c,
                                                       int accumulate, float* __restrict__ part,
@@ -125,10 +177,18 @@ __global__ __launch_bounds__(kThreads, 1) void anchor_bf16(const TIn* __restrict
   constexpr int KBLK = kBC * RB / 1024;   // 1 KB direct-to-LDS blocks per K tile
   constexpr int LK = KBLK > kWaves ? KBLK / kWaves : 1;  // K blocks per loading wave
   constexpr int KW = KBLK / LK;           // waves that load K (4 for fp8, D = 64)
-  constexpr int LV = kBC * D * 2 / 1024 / kWaves;        // V^T blocks per wave
+  static_assert(!P8 || F8, "fp8 P needs fp8 inputs");
+  using VE = std::conditional_t<P8, uint8_t, uint16_t>;  // V^T element: e4m3 or bf16
+  constexpr int VES = sizeof(VE);
+  constexpr int VBLK = kBC * D * VES / 1024;              // 1 KB blocks per V^T tile
+  constexpr int LV = VBLK > kWaves ? VBLK / kWaves : 1;    // V^T blocks per loading wave
+  constexpr int VW = VBLK / LV;                            // waves that load V^T
+  constexpr int VCH = kBC * VES / 16;     // 16-byte chunks per V^T row
+  constexpr int VRPB = 1024 / (kBC * VES);  // V^T rows per block
   constexpr int RPB = 1024 / RB;          // K rows per block
   constexpr uint32_t kTileBytes = kBC * RB;
   using QOp = std::conditional_t<F8, u32x8, u32x4>;
+  const VE* __restrict__ VT = reinterpret_cast<const VE*>(VTv);
   // Four separate LDS arrays rather than two [2][...] ones: the compiler then
   // knows that the direct-to-LDS loads filling one buffer do not alias the
   // reads of the other, and does not make every LDS read wait for them.
@@ -136,10 +196,10 @@ __global__ __launch_bounds__(kThreads, 1) void anchor_bf16(const TIn* __restrict
   __shared__ __attribute__((aligned(16))) TIn Ks1[kBC * D];
   __shared__ __attribute__((aligned(16))) TIn Ks2[kBC * D];
   __shared__ __attribute__((aligned(16))) TIn Ks3[kBC * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs0[kBC * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs1[kBC * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs2[kBC * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs3[kBC * D];
+  __shared__ __attribute__((aligned(16))) VE Vs0[kBC * D];
+  __shared__ __attribute__((aligned(16))) VE Vs1[kBC * D];
+  __shared__ __attribute__((aligned(16))) VE Vs2[kBC * D];
+  __shared__ __attribute__((aligned(16))) VE Vs3[kBC * D];
   // buffer b of each tensor: a compile-time b names one array, which lets the
   // compiler keep LDS reads of one buffer independent of the DMA into another;
   // a run-time b (rare edge iterations) selects among them
@@ -155,7 +215,7 @@ __global__ __launch_bounds__(kThreads, 1) void anchor_bf16(const TIn* __restrict
       else return Ks3;
     }
   };
-  auto vbuf = [&](auto b) -> uint16_t* {
+  auto vbuf = [&](auto b) -> VE* {
     if constexpr (std::is_integral_v<decltype(b)>) {
       const int x = b & 3;
       return x == 0 ? Vs0 : x == 1 ? Vs1 : x == 2 ? Vs2 : Vs3;
@@ -214,9 +274,10 @@ __global__ __launch_bounds__(kThreads, 1) void anchor_bf16(const TIn* __restrict
   // wave w fills 1 KB LDS block bw = L*w + i in lane order. K tiles hold RPB key
   // rows of RB bytes per block (4 x 256 B for bf16 D=128, 8 x 128 B for bf16
   // D=64 and fp8 D=128, 16 x 64 B for fp8 D=64): lane l lands in row
-  // RPB bw + l/CH, physical chunk l%CH. V^T tiles hold 8 feature rows of 128 B
-  // (64 bf16 keys) per block: lane l lands in row 8bw + l/8, physical chunk l%8.
-  // Each lane fetches the logical chunk that the swizzle puts there.
+  // RPB bw + l/CH, physical chunk l%CH. V^T tiles hold VRPB feature rows per
+  // block (8 x 128 B of 64 bf16 keys, or 16 x 64 B of 64 fp8 keys): lane l lands
+  // in row VRPB bw + l/VCH, physical chunk l%VCH. Each lane fetches the logical
+  // chunk that the swizzle puts there.
   uint32_t goff_k[LK], goff_v[LV];
 #pragma unroll
   for (int i = 0; i < LK; ++i) {
@@ -225,10 +286,11 @@ __global__ __launch_bounds__(kThreads, 1) void anchor_bf16(const TIn* __restrict
   }
 #pragma unroll
   for (int i = 0; i < LV; ++i) {
-    const int vd = (LV * wave + i) * 8 + (lane >> 3), vpc = lane & 7;
-    goff_v[i] = ((uint32_t)vd * n_pad + ((vpc ^ vt_swz(vd)) * 8)) * 2;
+    const int vd = (LV * wave + i) * VRPB + lane / VCH, vpc = lane % VCH;
+    const int sw = P8 ? vt8_swz(vd) : vt_swz(vd);
+    goff_v[i] = (uint32_t)vd * n_pad * VES + (uint32_t)(vpc ^ sw) * 16;
   }
-  const uint32_t vt_head_bytes = (uint32_t)D * n_pad * 2;
+  const uint32_t vt_head_bytes = (uint32_t)D * n_pad * VES;
   // issue K (or V^T) tile j into LDS buffer buf (completion: wait_all_memory + barrier).
   // No branch on the tile index: a tile past the end gets a zero-size descriptor,
   // so its loads touch no memory and fill LDS with zeros that nothing reads.
@@ -242,11 +304,13 @@ __global__ __launch_bounds__(kThreads, 1) void anchor_bf16(const TIn* __restrict
       buf_load16_lds(kr, goff_k[i], kbuf(buf_c) + (LK * wave + i) * (1024 / ES));
   };
   auto load_v = [&](int j, auto buf_c) {
-    const uint32_t done = (uint32_t)j * kBC * 2;
+    if (VW < kWaves && wave >= VW) return;  // wave-uniform
+    const uint32_t done = (uint32_t)j * kBC * VES;
     const uint32_t left = j * kBC < n_pad ? vt_head_bytes - done : 0u;
     const rsrc_t vr = make_rsrc_uniform(VT + (size_t)bh * D * n_pad + (size_t)j * kBC, left);
 #pragma unroll
-    for (int i = 0; i < LV; ++i) buf_load16_lds(vr, goff_v[i], vbuf(buf_c) + (LV * wave + i) * 512);
+    for (int i = 0; i < LV; ++i)
+      buf_load16_lds(vr, goff_v[i], vbuf(buf_c) + (LV * wave + i) * (1024 / VES));
   };
 
   // S^T operand A (key rows): lane reads row kb*32 + r, logical chunks
@@ -261,15 +325,24 @@ __global__ __launch_bounds__(kThreads, 1) void anchor_bf16(const TIn* __restrict
   // d = 32b + vrow, vrow = 16((r>>2)&1) + 4(r>>3) + (r&3), so each lane ends with
   // 16 consecutive output features; its 8 keys of k-step ks are logical chunk
   // 2ks + h of that row
+  // (bf16 V^T); for e4m3 V^T its 32 keys of the tile are logical chunks 2h and 2h + 1
   const int vrow = 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);
   int voff[4];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) voff[ks] = vrow * kBC + (((2 * ks + h) ^ vt_swz(vrow)) * 8);
+  for (int ks = 0; ks < 4; ++ks) {
+    if constexpr (P8) voff[ks] = vrow * kBC + (((2 * h + (ks & 1)) ^ vt8_swz(vrow)) * 16);
+    else voff[ks] = vrow * kBC + (((2 * ks + h) ^ vt_swz(vrow)) * 8);
+  }
 
   f32x16 acc[ND];
 #pragma unroll
   for (int b = 0; b < ND; ++b) acc[b] = (f32x16){};
   float m_run = -INFINITY, l_run = 0.f;
+  // fp8-P mode: the row sum is a fifth accumulator, ones^T P^T on the matrix
+  // cores (every row of it holds the query's sum of the rounded P), rescaled
+  // with the others; the bf16 mode sums on the VALU into l_run
+  f32x16 acc_l = (f32x16){};
+  const u32x4 ones8 = {0x38383838u, 0x38383838u, 0x38383838u, 0x38383838u};  // e4m3 1.0
   const int ntiles = (N + kBC - 1) / kBC;
   const bool ragged = (N % kBC) != 0;
   // key tiles [t0, t1) of this workgroup
@@ -298,19 +371,32 @@ __global__ __launch_bounds__(kThreads, 1) void anchor_bf16(const TIn* __restrict
   };
   // O^T += V^T P^T for the tile held in V buffer VB; k-slot s of half h is
   // key 16ks + 8(s>>2) + 4h + (s&3)
+  // (bf16 P; for e4m3 P, pb[0..1] is the 32-byte operand of the whole tile)
   auto pv_tile = [&](auto vb_c, const u32x4* pb) {
-    const uint16_t* Vb = vbuf(vb_c);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    const VE* Vb = vbuf(vb_c);
+    if constexpr (P8) {
 #pragma unroll
       for (int b = 0; b < ND; ++b) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(&Vb[b * 32 * kBC + voff[ks]]);
-        acc[b] = mfma32x32x16(a, pb[ks], acc[b]);
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(&Vb[b * 32 * kBC + voff[0]]);
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(&Vb[b * 32 * kBC + voff[1]]);
+        acc[b] = mfma32x32x64_fp8(concat(a0, a1), concat(pb[0], pb[1]), acc[b]);
+      }
+      acc_l = mfma32x32x64_fp8(concat(ones8, ones8), concat(pb[0], pb[1]), acc_l);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+        for (int b = 0; b < ND; ++b) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(&Vb[b * 32 * kBC + voff[ks]]);
+          acc[b] = mfma32x32x16(a, pb[ks], acc[b]);
+        }
       }
     }
   };
-  // online softmax of S^T for tile j: returns the bf16 P^T operands in pb and
-  // the factor alpha by which the accumulator must be rescaled (1 if none)
+  // online softmax of S^T for tile j: returns the P^T operands in pb (bf16:
+  // four 16-byte k-steps; e4m3: pb[kb] holds score elements 0..15 of 32-key
+  // block kb as bytes) and the factor alpha by which the accumulator must be
+  // rescaled (1 if none)
   auto softmax = [&](f32x16* s, u32x4* pb, int j, bool mask) -> float {
     if (mask) {
       asm volatile("");
@@ -344,20 +430,27 @@ __global__ __launch_bounds__(kThreads, 1) void anchor_bf16(const TIn* __restrict
       float p[16];
 #pragma unroll
       for (int x = 0; x < 16; ++x) p[x] = exp2_fast(fmaf(s[kb][x], c, -m_run));
+      if constexpr (P8) {
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int qq = half * 8;
-        pb[kb * 2 + half] = (u32x4){pack_bf16(p[qq + 0], p[qq + 1]), pack_bf16(p[qq + 2], p[qq + 3]),
-                                    pack_bf16(p[qq + 4], p[qq + 5]), pack_bf16(p[qq + 6], p[qq + 7])};
+        for (int w = 0; w < 4; ++w) pb[kb][w] = pack_fp8x4(p[4 * w], p[4 * w + 1], p[4 * w + 2], p[4 * w + 3]);
+      } else {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int qq = half * 8;
+          pb[kb * 2 + half] = (u32x4){pack_bf16(p[qq + 0], p[qq + 1]), pack_bf16(p[qq + 2], p[qq + 3]),
+                                      pack_bf16(p[qq + 4], p[qq + 5]), pack_bf16(p[qq + 6], p[qq + 7])};
+        }
       }
     }
     // the row sum adds the same rounded values the MFMA consumes (4 chains)
-    float l4[4] = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (!P8) {
+      float l4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+      for (int x = 0; x < 4; ++x)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) l4[ks] = add_bf16x2(pb[ks][x], l4[ks]);
-    l_run += (l4[0] + l4[1]) + (l4[2] + l4[3]);
+        for (int ks = 0; ks < 4; ++ks) l4[ks] = add_bf16x2(pb[ks][x], l4[ks]);
+      l_run += (l4[0] + l4[1]) + (l4[2] + l4[3]);
+    }
     return alpha;
   };
   auto rescale = [&](float alpha) {
@@ -367,6 +460,7 @@ __global__ __launch_bounds__(kThreads, 1) void anchor_bf16(const TIn* __restrict
       asm volatile("");
 #pragma unroll
       for (int b = 0; b < ND; ++b) acc[b] *= alpha;
+      if constexpr (P8) acc_l *= alpha;
     }
   };
 
@@ -412,10 +506,11 @@ __global__ __launch_bounds__(kThreads, 1) void anchor_bf16(const TIn* __restrict
     if (STEADY || jl > 0) pv_tile(shifted(S3{}), p_prev);
     f32x16 s_next[2];
     if (STEADY || j + 1 < t1) s_tile(shifted(S1{}), s_next);
-    asm volatile("" ::"v"(p_cur[0]), "v"(p_cur[1]), "v"(p_cur[2]), "v"(p_cur[3]), "v"(l_run));
+    if constexpr (P8) asm volatile("" ::"v"(p_cur[0]), "v"(p_cur[1]), "v"(l_run));
+    else asm volatile("" ::"v"(p_cur[0]), "v"(p_cur[1]), "v"(p_cur[2]), "v"(p_cur[3]), "v"(l_run));
     rescale(alpha);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) p_prev[ks] = p_cur[ks];
+    for (int ks = 0; ks < (P8 ? 2 : 4); ++ks) p_prev[ks] = p_cur[ks];
     s_cur[0] = s_next[0];
     s_cur[1] = s_next[1];
     if (!first) {
@@ -457,7 +552,7 @@ __global__ __launch_bounds__(kThreads, 1) void anchor_bf16(const TIn* __restrict
 
   if (piece >= 0) {
     // partial result of a key range: unnormalised O, running max and row sum
-    const float l_tot = add_halves(l_run);
+    const float l_tot = P8 ? acc_l[0] : add_halves(l_run);
     const int row = wave * 32 + r;
     float* po = part + ((size_t)piece * kBR + row) * D;
 #pragma unroll
@@ -475,7 +570,7 @@ __global__ __launch_bounds__(kThreads, 1) void anchor_bf16(const TIn* __restrict
   }
 
   // epilogue: lane (query r, half h) holds features 32b + 16h + 0..15 of block b
-  const float l_tot = add_halves(l_run);
+  const float l_tot = P8 ? acc_l[0] : add_halves(l_run);
   const float inv = 1.0f / l_tot;
   if (qrow >= N) return;
 #pragma unroll
@@ -601,21 +696,23 @@ struct AnchorLayout {
   size_t vt_bytes, part_off, ml_off, total;
   int pieces_cap;
 };
-AnchorLayout anchor_layout(const hla_dims& d) {
+// fp8_p: the fp8-P mode, whose V^T copy takes one byte per element (else two)
+AnchorLayout anchor_layout(const hla_dims& d, bool fp8_p) {
   AnchorLayout L;
   const int64_t BH = d.B * d.H, N = d.N, D = d.D;
   const int64_t n_pad = (N + kBC - 1) / kBC * kBC;
   const int64_t nqb = (N + kBR - 1) / kBR, ntiles = n_pad / kBC;
   const int64_t cap = BH * nqb * ntiles;
   L.pieces_cap = int(cap < kMaxPieces ? cap : kMaxPieces);
-  L.vt_bytes = align_up(size_t(BH * D * n_pad * 2), 256);
+  const int64_t ves = fp8_p ? 1 : 2;  // V^T bytes per element
+  L.vt_bytes = align_up(size_t(BH * D * n_pad * ves), 256);
   L.part_off = L.vt_bytes;
   L.ml_off = L.part_off + align_up(size_t(L.pieces_cap) * kBR * D * 4, 256);
   L.total = L.ml_off + align_up(size_t(L.pieces_cap) * kBR * 2 * 4, 256);
   return L;
 }
 
-template <int D, typename TIn>
+template <int D, typename TIn, bool P8>
 hipError_t launch_d(const hla_dims& d, const void* q, const void* k, const void* v, const void* g,
                     void* out, int accumulate, float scale, void* ws, hipStream_t stream) {
   const int BH = int(d.B * d.H), N = int(d.N);
@@ -624,9 +721,9 @@ hipError_t launch_d(const hla_dims& d, const void* q, const void* k, const void*
   const int nqb = (N + kBR - 1) / kBR;
   const int total = BH * nqb;
   const float c = scale * kLog2e;
-  const AnchorLayout L = anchor_layout(d);
+  const AnchorLayout L = anchor_layout(d, P8);
   char* w = reinterpret_cast<char*>(ws);
-  uint16_t* vt = reinterpret_cast<uint16_t*>(w);
+  void* vt = w;
   float* part = reinterpret_cast<float*>(w + L.part_off);
   float* part_ml = reinterpret_cast<float*>(w + L.ml_off);
   // Workgroups run in batches of one per CU. The query blocks of an
@@ -663,19 +760,23 @@ hipError_t launch_d(const hla_dims& d, const void* q, const void* k, const void*
   }
   const int nmain = total - tail;
   const int grid = nmain + tail * split;
-  hipLaunchKernelGGL((anchor_pack_vt<D, TIn>), dim3(n_pad / kBC, BH), dim3(256), 0, stream,
-                     reinterpret_cast<const TIn*>(v), vt, N, n_pad);
+  if constexpr (P8)
+    hipLaunchKernelGGL((anchor_pack_vt8<D>), dim3(n_pad / kBC, BH), dim3(256), 0, stream,
+                       reinterpret_cast<const uint8_t*>(v), reinterpret_cast<uint8_t*>(vt), N, n_pad);
+  else
+    hipLaunchKernelGGL((anchor_pack_vt<D, TIn>), dim3(n_pad / kBC, BH), dim3(256), 0, stream,
+                       reinterpret_cast<const TIn*>(v), reinterpret_cast<uint16_t*>(vt), N, n_pad);
   const TIn* Qp = reinterpret_cast<const TIn*>(q);
   const TIn* Kp = reinterpret_cast<const TIn*>(k);
   const TIn* Gp = reinterpret_cast<const TIn*>(g);
   if (d.out_dtype == HLA_F32) {
-    hipLaunchKernelGGL((anchor_bf16<D, true, TIn>), dim3(grid), dim3(kThreads), 0, stream, Qp, Kp,
+    hipLaunchKernelGGL((anchor_bf16<D, true, TIn, P8>), dim3(grid), dim3(kThreads), 0, stream, Qp, Kp,
                        Gp, vt, out, N, n_pad, nqb, nmain, split, c, accumulate, part, part_ml);
     if (tail > 0)
       hipLaunchKernelGGL((anchor_combine<D, true, TIn>), dim3(tail * (D / 8)), dim3(256), 0, stream,
                          part, part_ml, Gp, out, N, nqb, nmain, split, accumulate);
   } else {
-    hipLaunchKernelGGL((anchor_bf16<D, false, TIn>), dim3(grid), dim3(kThreads), 0, stream, Qp, Kp,
+    hipLaunchKernelGGL((anchor_bf16<D, false, TIn, P8>), dim3(grid), dim3(kThreads), 0, stream, Qp, Kp,
                        Gp, vt, out, N, n_pad, nqb, nmain, split, c, accumulate, part, part_ml);
     if (tail > 0)
       hipLaunchKernelGGL((anchor_combine<D, false, TIn>), dim3(tail * (D / 8)), dim3(256), 0,
@@ -688,18 +789,25 @@ hipError_t launch_d(const hla_dims& d, const void* q, const void* k, const void*
 
 size_t anchor_workspace_bytes(const hla_dims& d) {
   if (d.in_dtype == HLA_F32) return 0;
-  return anchor_layout(d).total;
+  return anchor_layout(d, false).total;
 }
 
 hipError_t launch_anchor_bf16(const hla_dims& d, const void* q, const void* k, const void* v,
                               const void* g, void* out, int accumulate, float scale, void* ws,
-                              hipStream_t stream) {
+                              hipStream_t stream, bool fp8_p) {
   if (d.in_dtype == HLA_FP8_E4M3) {
-    if (d.D == 128) return launch_d<128, uint8_t>(d, q, k, v, g, out, accumulate, scale, ws, stream);
-    return launch_d<64, uint8_t>(d, q, k, v, g, out, accumulate, scale, ws, stream);
+    if (fp8_p) {
+      if (d.D == 128)
+        return launch_d<128, uint8_t, true>(d, q, k, v, g, out, accumulate, scale, ws, stream);
+      return launch_d<64, uint8_t, true>(d, q, k, v, g, out, accumulate, scale, ws, stream);
+    }
+    if (d.D == 128)
+      return launch_d<128, uint8_t, false>(d, q, k, v, g, out, accumulate, scale, ws, stream);
+    return launch_d<64, uint8_t, false>(d, q, k, v, g, out, accumulate, scale, ws, stream);
   }
-  if (d.D == 128) return launch_d<128, uint16_t>(d, q, k, v, g, out, accumulate, scale, ws, stream);
-  return launch_d<64, uint16_t>(d, q, k, v, g, out, accumulate, scale, ws, stream);
+  if (d.D == 128)
+    return launch_d<128, uint16_t, false>(d, q, k, v, g, out, accumulate, scale, ws, stream);
+  return launch_d<64, uint16_t, false>(d, q, k, v, g, out, accumulate, scale, ws, stream);
 }
 
 }  // namespace hla

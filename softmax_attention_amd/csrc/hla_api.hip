@@ -212,11 +212,12 @@ hla_status hla_linear_write_gated_fwd(const hla_dims* d, const void* q, const vo
                        stream);
 }
 
-hla_status hla_softmax_anchor_fwd(const hla_dims* d, const void* q, const void* k, const void* v,
-                                  const void* g, void* out, int accumulate, float scale,
-                                  void* workspace, size_t workspace_bytes, void* stream) {
+static hla_status anchor_common(const hla_dims* d, const void* q, const void* k, const void* v,
+                                const void* g, void* out, int accumulate, float scale,
+                                void* workspace, size_t workspace_bytes, void* stream, bool fp8_p) {
   hla_status st = check_dims(d);
   if (st != HLA_OK) return st;
+  if (fp8_p && d->in_dtype != HLA_FP8_E4M3) return HLA_ERR_UNSUPPORTED;
   if (!isfinite(scale) || scale <= 0.f || (accumulate != 0 && accumulate != 1))
     return HLA_ERR_BAD_ARG;
   if (empty(d)) return HLA_OK;
@@ -230,8 +231,23 @@ hla_status hla_softmax_anchor_fwd(const hla_dims* d, const void* q, const void* 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   clear_pending_error();
   if (d->in_dtype != HLA_F32)
-    return from_hip(launch_anchor_bf16(*d, q, k, v, g, out, accumulate, scale, workspace, s));
+    return from_hip(launch_anchor_bf16(*d, q, k, v, g, out, accumulate, scale, workspace, s, fp8_p));
   return from_hip(launch_anchor_f32(*d, q, k, v, g, out, accumulate, scale, s));
+}
+
+hla_status hla_softmax_anchor_fwd(const hla_dims* d, const void* q, const void* k, const void* v,
+                                  const void* g, void* out, int accumulate, float scale,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  return anchor_common(d, q, k, v, g, out, accumulate, scale, workspace, workspace_bytes, stream,
+                       false);
+}
+
+hla_status hla_softmax_anchor_fp8p_fwd(const hla_dims* d, const void* q, const void* k,
+                                       const void* v, const void* g, void* out, int accumulate,
+                                       float scale, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  return anchor_common(d, q, k, v, g, out, accumulate, scale, workspace, workspace_bytes, stream,
+                       true);
 }
 
 hla_status hla_hybrid_stack_fwd(const hla_dims* d, int n_layers, const int32_t* kinds,

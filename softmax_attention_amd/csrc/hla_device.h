@@ -173,6 +173,19 @@ __device__ __forceinline__ u32x4 fp8x8_to_bf16(u32x2 w) {
                  __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d)};
 }
 
+// Four floats -> four OCP e4m3 bytes (v_cvt_pk_fp8_f32: round to nearest even),
+// a in byte 0 .. d in byte 3.
+__device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+// four e4m3 bytes -> four bf16 as two packed pairs (bytes 0,1 then 2,3), exact
+__device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+  return (u32x2){__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
+}
+
 // Eight consecutive elements of a bf16 or fp8 tensor as eight bf16 values.
 template <typename T>
 __device__ __forceinline__ u32x4 load8_bf16(const T* p) {

@@ -53,9 +53,10 @@ hipError_t launch_linear_f32(const hla_dims& d, const void* q, const void* k, co
                              void* ws, const LinearPlan& plan, hipStream_t stream);
 // Workspace of the bf16 anchor: V repacked as V^T per head, keys padded to 64.
 size_t anchor_workspace_bytes(const hla_dims& d);
+// fp8_p: P rounded to e4m3 and P V on the fp8 matrix cores (fp8 inputs only)
 hipError_t launch_anchor_bf16(const hla_dims& d, const void* q, const void* k, const void* v,
                               const void* g, void* out, int accumulate, float scale, void* ws,
-                              hipStream_t stream);
+                              hipStream_t stream, bool fp8_p = false);
 hipError_t launch_anchor_f32(const hla_dims& d, const void* q, const void* k, const void* v,
                              const void* g, void* out, int accumulate, float scale,
                              hipStream_t stream);

@@ -4,7 +4,9 @@
 // LDS 16-byte read rate. They back the hardware figures the kernels' rooflines
 // are discussed against. Built into a library of its own (libhla_probes.so),
 // separate from the attention library; callers pass device buffers and a
-// stream, and time the launches themselves.
+// stream, and time the launches themselves. hla_probe_cvt_fp8 runs the
+// attention kernels' own fp32 -> e4m3 rounding (pack_fp8x4) on given values, so
+// that tests can pin it to the format's definition.
 //
 // Every probe writes one float per thread to `out` (so the compiler keeps the
 // work) and, from thread 0 of each workgroup, the workgroup's elapsed shader
@@ -13,6 +15,8 @@
 // out >= grid * 512 floats, clk >= grid int64.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include "hla_device.h"
 
 typedef __bf16 bf16x8_p __attribute__((ext_vector_type(8)));
 typedef float f32x16_p __attribute__((ext_vector_type(16)));
@@ -129,6 +133,13 @@ __global__ __launch_bounds__(512, 1) void probe_lds(float* out, long long* clk, 
   if (tid == 0) clk[blockIdx.x] = t1 - t0;
 }
 
+// out[i] = e4m3 bytes of in[4i .. 4i+3], as the anchor packs its probabilities
+__global__ __launch_bounds__(256) void probe_cvt_fp8(const float* __restrict__ in,
+                                                      uint32_t* __restrict__ out, int n4) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n4) out[i] = hla::pack_fp8x4(in[4 * i], in[4 * i + 1], in[4 * i + 2], in[4 * i + 3]);
+}
+
 }  // namespace
 
 extern "C" {
@@ -157,6 +168,14 @@ int hla_probe_exp(int grid, int iters, float* out, long long* clk, void* stream)
   if (grid <= 0 || iters <= 0 || !out || !clk) return 1;
   hipLaunchKernelGGL(probe_exp, dim3(grid), dim3(512), 0, reinterpret_cast<hipStream_t>(stream), out,
                      clk, iters);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// n4 groups of four floats -> n4 words of four e4m3 bytes
+int hla_probe_cvt_fp8(const float* in, uint32_t* out, int n4, void* stream) {
+  if (n4 <= 0 || !in || !out) return 1;
+  hipLaunchKernelGGL(probe_cvt_fp8, dim3((n4 + 255) / 256), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream), in, out, n4);
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 

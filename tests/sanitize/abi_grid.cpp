@@ -78,6 +78,9 @@ int main(void) {
                      ne, "hla_linear_fwd_noalloc", &d);
               expect(hla_softmax_anchor_fwd(&d, q, FAKE, FAKE, FAKE, out, acc, scale, ws, wsb, NULL),
                      ne, "hla_softmax_anchor_fwd", &d);
+              expect(hla_softmax_anchor_fp8p_fwd(&d, q, FAKE, FAKE, FAKE, out, acc, scale, ws, wsb,
+                                                 NULL),
+                     ne, "hla_softmax_anchor_fp8p_fwd", &d);
               const void* qa[2] = {bad == 0 ? NULL : FAKE, FAKE};
               expect(hla_hybrid_stack_fwd(&d, bad == 3 ? 0 : 2, kinds, qa, ptrs, ptrs, ptrs, out, eps,
                                           scale, ws, wsb, NULL),

@@ -49,6 +49,11 @@ def sm(d, q=FAKE, k=FAKE, v=FAKE, g=FAKE, out=FAKE, acc=0, scale=0.1, ws=FAKE, w
                                           out, acc, scale, ws, wsb, None)
 
 
+def sm8p(d, q=FAKE, k=FAKE, v=FAKE, g=FAKE, out=FAKE, acc=0, scale=0.1, ws=FAKE, wsb=1 << 40):
+    return hla.lib.hla_softmax_anchor_fp8p_fwd(ctypes.byref(d) if d is not None else None, q, k, v,
+                                               g, out, acc, scale, ws, wsb, None)
+
+
 def stack(d, n=2, kinds=(0, 1), ptrs=None, x=FAKE, eps=1e-6, scale=0.1, ws=FAKE, wsb=1 << 40):
     arr = ctypes.c_void_p * max(n, 1)
     p = ptrs if ptrs is not None else [FAKE] * max(n, 1)
@@ -100,7 +105,7 @@ def test_c_client_source_compiles():
 
 
 def test_version_and_status_strings():
-    assert hla.hla_abi_version() == 4
+    assert hla.hla_abi_version() == 5
     for code, name in hla.STATUS.items():
         assert hla.hla_status_str(code) == name
     assert hla.hla_status_str(99) == "HLA_UNKNOWN"
@@ -187,6 +192,28 @@ def test_fp8_inputs():
             hla.hla_softmax_anchor_workspace_bytes(dims(N=N, D=D, i=BF16))
     assert sm(d, ws=None) == NULLP
     assert sm(d, wsb=hla.hla_softmax_anchor_workspace_bytes(d) - 1) == WS
+
+
+def test_fp8p_anchor_errors():
+    # the fp8-probability anchor takes fp8 inputs only, and otherwise checks its
+    # arguments as the anchor does; its workspace is the anchor's
+    assert sm8p(None) == NULLP
+    assert sm8p(dims(i=BF16)) == UNSUP
+    assert sm8p(dims(i=F32, o=F32, D=32)) == UNSUP
+    assert sm8p(dims(B=-1, i=FP8)) == SHAPE
+    assert sm8p(dims(i=FP8, D=96)) == UNSUP
+    assert sm8p(dims(i=FP8, o=FP8)) == UNSUP
+    d = dims(i=FP8)
+    for p in ("q", "k", "v", "g", "out"):
+        assert sm8p(d, **{p: None}) == NULLP, p
+        assert sm8p(d, **{p: ODD}) == ALIGN, p
+    for s_ in (0.0, -0.1, float("nan"), float("inf")):
+        assert sm8p(d, scale=s_) == BADARG
+    assert sm8p(d, acc=3) == BADARG
+    assert sm8p(d, ws=None) == NULLP
+    assert sm8p(d, ws=ODD) == ALIGN
+    assert sm8p(d, wsb=hla.hla_softmax_anchor_workspace_bytes(d) - 1) == WS
+    assert sm8p(dims(N=0, i=FP8), q=None, k=None, v=None, g=None, out=None, ws=None, wsb=0) == OK
 
 
 def test_softmax_argument_errors():

@@ -15,7 +15,8 @@ stack).
 --profile {anchor,linear,step,copy} runs just that piece a few times, for
 rocprofv3 kernel traces and counter passes (copy: a plain device copy of known
 size that calibrates FETCH_SIZE / WRITE_SIZE); anchor_fp8, linear_fp8 and
-step_fp8 do the same on fp8 (e4m3) copies of the inputs; linear_wg runs the
+step_fp8 do the same on fp8 (e4m3) copies of the inputs, anchor_fp8p the
+e4m3-probability anchor on them; linear_wg runs the
 write-gated linear layer; attnres runs the block-attention-residual routing at
 the stack shape with two blocks; tiny runs the tiny fp32 pair. Two more print
 JSON lines of their own: probes (matrix-core rate and shader clock for operand
@@ -93,6 +94,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--profile", default=None,
                     choices=["anchor", "linear", "step", "copy", "anchor_fp8", "linear_fp8", "step_fp8",
+                             "anchor_fp8p",
                              "attnres", "linear_wg", "tiny", "probes", "cache_states"])
     ap.add_argument("--iters", type=int, default=5, help="launches per --profile run")
     ap.add_argument("--sweep", action="store_true",
@@ -242,9 +244,10 @@ def main():
         return
 
     sets = [gpu_inputs(w, s, torch) for s in range(2)]
-    if args.profile and args.profile.endswith("_fp8"):
+    if args.profile and (args.profile.endswith("_fp8") or args.profile == "anchor_fp8p"):
         sets = [[t.to(torch.float8_e4m3fn) for t in s_] for s_ in sets]
-        args.profile = args.profile[:-4]
+        if args.profile.endswith("_fp8"):
+            args.profile = args.profile[:-4]
     outs = [torch.empty(sets[0][0].shape, dtype=torch.bfloat16, device=dev) for _ in range(2)]
     ws = hla.linear_workspace(sets[0][0], torch.bfloat16)
     ws_a = hla.anchor_workspace(sets[0][0], torch.bfloat16)
@@ -256,6 +259,10 @@ def main():
     def anchor(i):
         q, k, v, g = sets[i % 2]
         hla.hla_softmax_anchor_fwd(q, k, v, g, out=outs[1], scale=w.scale, workspace=ws_a)
+
+    def anchor_fp8p(i):
+        q, k, v, g = sets[i % 2]
+        hla.hla_softmax_anchor_fp8p_fwd(q, k, v, g, out=outs[1], scale=w.scale, workspace=ws_a)
 
     logits = None
     if args.profile == "linear_wg":
@@ -271,7 +278,7 @@ def main():
         # args.warmup untimed launches first, then args.iters; a trace summary
         # drops the first args.warmup launches of each kernel
         fn = {"anchor": [anchor], "linear": [linear], "step": [linear, anchor],
-              "linear_wg": [linear_wg]}[args.profile]
+              "linear_wg": [linear_wg], "anchor_fp8p": [anchor_fp8p]}[args.profile]
         for i in range(args.warmup + args.iters):
             for f in fn:
                 f(i)

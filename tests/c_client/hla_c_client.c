@@ -43,11 +43,12 @@ static int read_file(const char* dir, const char* name, void* buf, size_t n) {
 
 int main(int argc, char** argv) {
   if (argc != 9) {
-    fprintf(stderr, "usage: %s linear|softmax B H N D in_dtype out_dtype DIR\n", argv[0]);
+    fprintf(stderr, "usage: %s linear|softmax|softmax_fp8p B H N D in_dtype out_dtype DIR\n", argv[0]);
     return 2;
   }
   const int is_linear = strcmp(argv[1], "linear") == 0;
-  if (!is_linear && strcmp(argv[1], "softmax") != 0) return 2;
+  const int is_fp8p = strcmp(argv[1], "softmax_fp8p") == 0;
+  if (!is_linear && !is_fp8p && strcmp(argv[1], "softmax") != 0) return 2;
   hla_dims d;
   d.B = atoll(argv[2]);
   d.H = atoll(argv[3]);
@@ -106,8 +107,12 @@ int main(int argc, char** argv) {
     }
     /* 1/sqrt(D) rounded once to float, as the Python binding passes it */
     const float scale = (float)(1.0 / sqrt((double)d.D));
-    st = hla_softmax_anchor_fwd(&d, dev[0], dev[1], dev[2], dev[3], out, 0, scale, ws, ws_bytes,
-                                (void*)stream);
+    if (is_fp8p)
+      st = hla_softmax_anchor_fp8p_fwd(&d, dev[0], dev[1], dev[2], dev[3], out, 0, scale, ws,
+                                       ws_bytes, (void*)stream);
+    else
+      st = hla_softmax_anchor_fwd(&d, dev[0], dev[1], dev[2], dev[3], out, 0, scale, ws, ws_bytes,
+                                  (void*)stream);
   }
   if (st != HLA_OK) {
     fprintf(stderr, "call returned %s\n", hla_status_str(st));

@@ -31,6 +31,7 @@ CASES = [
     ("softmax", (1, 2, 300, 64), torch.bfloat16, torch.float32),
     ("softmax", (2, 2, 129, 128), FP8, torch.bfloat16),
     ("softmax", (1, 1, 65, 32), torch.float32, torch.float32),
+    ("softmax_fp8p", (2, 2, 300, 128), FP8, torch.bfloat16),
 ]
 
 
@@ -59,13 +60,17 @@ def test_c_client_matches_oracle_and_binding(tmp_path, op, shape, ind, outd):
         ref = oracle.gated_linear(q, k, v, g, 1e-6)
     else:
         ref = oracle.gated_softmax(q, k, v, g, D ** -0.5)
-    tol = 1e-4 if ind == torch.float32 else 2e-2
+    # the e4m3-probability anchor has its own, derived bound (tests/test_gpu_fp8_pv.py);
+    # here its slab-relative error is held to the bar that file applies at 720p
+    tol = 1e-4 if ind == torch.float32 else (5e-2 if op == "softmax_fp8p" else 2e-2)
     assert oracle.max_rel_error(got.float(), ref) <= tol
 
     d = [t.to("cuda") for t in (q, k, v, g)]
     out = torch.empty(shape, dtype=outd, device="cuda")
     if op == "linear":
         hla.hla_linear_fwd(*d, out=out, eps=1e-6)
+    elif op == "softmax_fp8p":
+        hla.hla_softmax_anchor_fp8p_fwd(*d, out=out)
     else:
         hla.hla_softmax_anchor_fwd(*d, out=out)
     torch.cuda.synchronize()

@@ -505,23 +505,26 @@ def test_write_gated_full_720p():
 def test_graph_capture_replays_match_eager():
     # the calls enqueue kernels only (no allocation, no memset), so they can be
     # captured in a HIP graph; every replay must reproduce the eager result
-    # (linear, anchor, write-gated linear and the block-summary routing)
+    # (linear, anchor, write-gated linear, the block-summary routing and the
+    # e4m3-probability anchor on fp8 copies of the inputs)
     B, H, N, D = 1, 4, 1500, 128
     q, k, v, g = (t.to(DEV) for t in make((B, H, N, D), 9000, torch.bfloat16))
     w = wlogits((B, H, N), 9100, torch.bfloat16).to(DEV)
     x, s0, s1 = (t.to(DEV) for t in custom((B, H, N, D), 9200, torch.float32, n=3))
     router = (custom((D, D), 9300, torch.float32, n=1)[0] * (2.0 / D ** 0.5)).to(torch.bfloat16).to(DEV)
     ws_l, ws_a = hla.linear_workspace(q), hla.anchor_workspace(q)
-    out_l, out_a, out_w = (torch.empty_like(q) for _ in range(3))
+    out_l, out_a, out_w, out_8 = (torch.empty_like(q) for _ in range(4))
     out_r = torch.empty_like(x)
+    q8, k8, v8, g8 = (t.to(FP8) for t in (q, k, v, g))
 
     def calls():
         hla.hla_linear_fwd(q, k, v, g, out=out_l, workspace=ws_l)
         hla.hla_softmax_anchor_fwd(q, k, v, g, out=out_a, workspace=ws_a)
         hla.hla_linear_write_gated_fwd(q, k, v, g, w, out=out_w, workspace=ws_l)
         hla.hla_attnres_route_fwd(x, [s0, s1], router, out=out_r)
+        hla.hla_softmax_anchor_fp8p_fwd(q8, k8, v8, g8, out=out_8, workspace=ws_a)
 
-    outs = (out_l, out_a, out_w, out_r)
+    outs = (out_l, out_a, out_w, out_r, out_8)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):

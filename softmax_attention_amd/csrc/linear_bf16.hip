@@ -505,6 +505,9 @@ __global__ __launch_bounds__(256, 2) void linear_out_bf16(const TIn* __restrict_
   constexpr int NU = D / 4 / EPL;        // runs per lane and token
   constexpr int JPU = NJ / NU;           // output fragments per run
   __shared__ u32x4 fr[NF * 64];
+  // fp8 gates take 256 values: sigma of each, computed once per workgroup with
+  // the same sigmoid, replaces an exp and a reciprocal per output element
+  __shared__ float sig_tab[F8 ? 256 : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bh = blockIdx.y;
@@ -550,6 +553,7 @@ __global__ __launch_bounds__(256, 2) void linear_out_bf16(const TIn* __restrict_
 #pragma unroll
   for (int i = 0; i < FPT; ++i)
     if (tid + 256 * i < NF * 64) fr[tid + 256 * i] = frv[i];
+  if constexpr (F8) sig_tab[tid] = sigmoid(fp8_to_f32((uint8_t)tid));  // 256 threads, 256 codes
   __syncthreads();
   if (grp * 16 >= N) return;
 
@@ -577,27 +581,25 @@ __global__ __launch_bounds__(256, 2) void linear_out_bf16(const TIn* __restrict_
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
         // run u: fragments JPU*u .. +JPU-1, 4 consecutive features each
-        float o[EPL], gf[EPL];
+        float o[EPL], sg[EPL];
 #pragma unroll
         for (int jj = 0; jj < JPU; ++jj)
 #pragma unroll
           for (int e = 0; e < 4; ++e) o[4 * jj + e] = acc[JPU * u + jj][e];
         if constexpr (F8) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const f32x4 f = fp8x4_to_f32(gv[u][q]);
+          for (int q = 0; q < 4; ++q)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) gf[4 * q + e] = f[e];
-          }
+            for (int e = 0; e < 4; ++e) sg[4 * q + e] = sig_tab[(gv[u][q] >> (8 * e)) & 0xffu];
         } else {
 #pragma unroll
           for (int p = 0; p < 4; ++p) {
-            gf[2 * p] = bf_lo(gv[u][p]);
-            gf[2 * p + 1] = bf_hi(gv[u][p]);
+            sg[2 * p] = sigmoid(bf_lo(gv[u][p]));
+            sg[2 * p + 1] = sigmoid(bf_hi(gv[u][p]));
           }
         }
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) o[e] = sigmoid(gf[e]) * (o[e] * rden);
+        for (int e = 0; e < EPL; ++e) o[e] = sg[e] * (o[e] * rden);
         const size_t off = base + (size_t)tok * D + 4 * EPL * u + EPL * g;
         if (OUT_F32) {
           float* dst = reinterpret_cast<float*>(out) + off;

@@ -630,6 +630,19 @@ def test_linear_fp8_every_code_matches_bf16_path():
     assert rel_err(a, b) <= 2.0 ** -6
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_linear_fp8_many_tiles_per_chunk(D):
+    # few heads, so each token chunk spans many state-pass tiles (256 tokens per
+    # tile at D = 64, 128 at D = 128) and a ragged last tile; bf16 and fp32 out
+    q, k, v, g = make((1, 2, 20011, D), 10400 + D, FP8)
+    ref = oracle.gated_linear(q, k, v, g, 1e-6)
+    for od in (torch.bfloat16, torch.float32):
+        got = run_linear(q, k, v, g, out_dtype=od)
+        e = rel_err(got, ref)
+        print(f"[fp8 linear N=20011 D={D} {od}] err {e:.3e}", flush=True)
+        assert e <= TOL[torch.bfloat16]
+
+
 def test_linear_fp8_binding_defaults_to_bf16_output():
     q, k, v, g = (t.to(DEV) for t in make((1, 2, 300, 64), 10300, FP8))
     out = hla.hla_linear_fwd(q, k, v, g)

@@ -488,11 +488,29 @@ __global__ __launch_bounds__(256) void linear_reduce_bf16(const char* __restrict
 // ---------------------------------------------------------------------------
 // 3. output pass
 // ---------------------------------------------------------------------------
-// Each wave takes 16 tokens at a time. Lane (n = lane & 15, g = lane >> 4) loads
-// 16 bytes of Q and of G of token n per run: features 32u + 8g .. +7 (bf16) or
-// 64u + 16g .. +15 (fp8, two k-steps). That is both its B-operand slice and, by
-// the fragment order (frag_pos), the feature run of its output values -- so Q,
-// G and O each move as 16-byte accesses with no shuffles.
+// Each wave takes 16 tokens at a time. Q and G of the group move from HBM as
+// whole 1 KB runs (64 lanes x 16 contiguous bytes per load instruction: four
+// 256-byte token rows, or eight 128-byte fp8 rows) and pass through the wave's
+// own LDS tile into the operand layout: lane (n = lane & 15, g = lane >> 4) then
+// holds 16 bytes of Q and of G of token n per run, features 32u + 8g .. +7
+// (bf16) or 64u + 16g .. +15 (fp8, two k-steps). That is both its B-operand
+// slice and, by the fragment order (frag_pos), the feature run of its output
+// values. A bf16 O goes back through the same tile and leaves as 1 KB runs too;
+// an fp32 O, or one added into, is stored from the operand layout (16-byte
+// accesses, 64 bytes per token and instruction).
+//
+// Tile slots are 16-byte chunks: chunk c of token row t (R chunks per row) sits
+// at t R + (c ^ ((t / (16 / R)) mod R)), so the 16 lanes of one 16-byte LDS
+// access (16 consecutive chunks of the 1 KB run, or one chunk of 16 rows) land
+// on 16 distinct bank groups.
+template <int R>
+__device__ __forceinline__ int out_slot(int t, int c) { return t * R + (c ^ ((t / (16 / R)) & (R - 1))); }
+
+// A wave's LDS tile is written by some lanes and read by others; a wave's LDS
+// instructions execute in issue order, so keeping the compiler from moving
+// them across this point is all the ordering needed.
+__device__ __forceinline__ void wave_lds_order() { asm volatile("" ::: "memory"); }
+
 template <int D, bool OUT_F32, typename TIn>
 __global__ __launch_bounds__(256, 2) void linear_out_bf16(const TIn* __restrict__ Q,
                                                        const TIn* __restrict__ G,
@@ -502,9 +520,14 @@ __global__ __launch_bounds__(256, 2) void linear_out_bf16(const TIn* __restrict_
   constexpr bool F8 = sizeof(TIn) == 1;
   constexpr int NT = D / 32, NJ = D / 16, NF = (NJ + 1) * NT;
   constexpr int EPL = 16 / sizeof(TIn);  // features per run
-  constexpr int NU = D / 4 / EPL;        // runs per lane and token
+  constexpr int NU = D / 4 / EPL;        // runs per lane and token (= load instructions per group)
   constexpr int JPU = NJ / NU;           // output fragments per run
+  constexpr int CPR = D * (int)sizeof(TIn) / 16;  // 16-byte chunks per token row of Q or G
+  constexpr int OCPR = D / 8;                     // 16-byte chunks per token row of a bf16 O
+  constexpr int TILE = 16 * CPR;                  // chunks of Q (or G) per group
+  static_assert(CPR == 4 * NU && 16 * OCPR <= 2 * TILE, "tile shapes");
   __shared__ u32x4 fr[NF * 64];
+  __shared__ u32x4 xs[4][2 * TILE];  // per wave: Q and G of its group, then its bf16 O
   // fp8 gates take 256 values: sigma of each, computed once per workgroup with
   // the same sigmoid, replaces an exp and a reciprocal per output element
   __shared__ float sig_tab[F8 ? 256 : 1];
@@ -517,6 +540,8 @@ __global__ __launch_bounds__(256, 2) void linear_out_bf16(const TIn* __restrict_
   const TIn* Gh = G + base;
   const int stride = gridDim.x * 4;
   int grp = blockIdx.x * 4 + wave;
+  u32x4* const tq = xs[wave];
+  u32x4* const tg = xs[wave] + TILE;
 
   // Buffer loads over the head: a token past N reads zeros without touching
   // memory, so every prefetch is issued unconditionally and the compiler can
@@ -526,11 +551,11 @@ __global__ __launch_bounds__(256, 2) void linear_out_bf16(const TIn* __restrict_
   const uint32_t head_bytes = (uint32_t)((size_t)N * D * sizeof(TIn));
   const rsrc_t Qr = make_rsrc(Qh, head_bytes), Gr = make_rsrc(Gh, head_bytes);
   auto load = [&](int gi, u32x4* qd, u32x4* gd) {
-    const uint32_t off = ((uint32_t)(gi * 16 + n) * D + EPL * g) * sizeof(TIn);
+    const uint32_t off = (uint32_t)gi * (uint32_t)(16 * D * sizeof(TIn)) + 16u * lane;
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-      qd[u] = buf_load16(Qr, off + 4 * EPL * u * sizeof(TIn));
-      gd[u] = buf_load16(Gr, off + 4 * EPL * u * sizeof(TIn));
+      qd[u] = buf_load16(Qr, off + 1024u * u);
+      gd[u] = buf_load16(Gr, off + 1024u * u);
     }
   };
 
@@ -557,7 +582,38 @@ __global__ __launch_bounds__(256, 2) void linear_out_bf16(const TIn* __restrict_
   __syncthreads();
   if (grp * 16 >= N) return;
 
-  auto compute = [&](int gi, const u32x4* qv, const u32x4* gv) __attribute__((always_inline)) {
+  // sigma of the EPL gate values of one run
+  auto gate_values = [&](const u32x4& gw, float* sg) __attribute__((always_inline)) {
+    if constexpr (F8) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sg[4 * q + e] = sig_tab[(gw[q] >> (8 * e)) & 0xffu];
+    } else {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        sg[2 * p] = sigmoid(bf_lo(gw[p]));
+        sg[2 * p + 1] = sigmoid(bf_hi(gw[p]));
+      }
+    }
+  };
+  auto compute = [&](int gi, const u32x4* qraw, const u32x4* graw) __attribute__((always_inline)) {
+    // the 1 KB runs into the tile, then this lane's operand chunks out of it
+    wave_lds_order();
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int k = 64 * u + lane, sl = out_slot<CPR>(k / CPR, k % CPR);
+      tq[sl] = qraw[u];
+      tg[sl] = graw[u];
+    }
+    wave_lds_order();
+    u32x4 qv[NU], gv[NU];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int sl = out_slot<CPR>(n, 4 * u + g);
+      qv[u] = tq[sl];
+      gv[u] = tg[sl];
+    }
     // Re-read the fragments from LDS every group: an opaque (always zero)
     // offset keeps the compiler from hoisting all of them into registers,
     // which would cost the occupancy this streaming loop needs.
@@ -577,7 +633,35 @@ __global__ __launch_bounds__(256, 2) void linear_out_bf16(const TIn* __restrict_
     const float rden = 1.0f / den;
 
     const int tok = gi * 16 + n;
-    if (tok < N) {
+    if (!OUT_F32 && !accumulate) {
+      // bf16 O through the tile: this lane's runs in, 1 KB runs out (rows past N
+      // are computed from zero Q and never stored)
+      wave_lds_order();
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        float o[EPL], sg[EPL];
+#pragma unroll
+        for (int jj = 0; jj < JPU; ++jj)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[4 * jj + e] = acc[JPU * u + jj][e];
+        gate_values(gv[u], sg);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[e] = sg[e] * (o[e] * rden);
+#pragma unroll
+        for (int x = 0; x < EPL / 8; ++x)
+          tq[out_slot<OCPR>(n, (4 * u + g) * (EPL / 8) + x)] =
+              (u32x4){pack_bf16(o[8 * x], o[8 * x + 1]), pack_bf16(o[8 * x + 2], o[8 * x + 3]),
+                      pack_bf16(o[8 * x + 4], o[8 * x + 5]), pack_bf16(o[8 * x + 6], o[8 * x + 7])};
+      }
+      wave_lds_order();
+      uint16_t* dst = reinterpret_cast<uint16_t*>(out) + base + (size_t)gi * 16 * D;
+#pragma unroll
+      for (int v = 0; v < OCPR / 4; ++v) {
+        const int k = 64 * v + lane, t = k / OCPR;
+        const u32x4 ov = tq[out_slot<OCPR>(t, k % OCPR)];
+        if (gi * 16 + t < N) stg16(dst + 8 * k, ov);
+      }
+    } else if (tok < N) {
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
         // run u: fragments JPU*u .. +JPU-1, 4 consecutive features each
@@ -586,18 +670,7 @@ __global__ __launch_bounds__(256, 2) void linear_out_bf16(const TIn* __restrict_
         for (int jj = 0; jj < JPU; ++jj)
 #pragma unroll
           for (int e = 0; e < 4; ++e) o[4 * jj + e] = acc[JPU * u + jj][e];
-        if constexpr (F8) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sg[4 * q + e] = sig_tab[(gv[u][q] >> (8 * e)) & 0xffu];
-        } else {
-#pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            sg[2 * p] = sigmoid(bf_lo(gv[u][p]));
-            sg[2 * p + 1] = sigmoid(bf_hi(gv[u][p]));
-          }
-        }
+        gate_values(gv[u], sg);
 #pragma unroll
         for (int e = 0; e < EPL; ++e) o[e] = sg[e] * (o[e] * rden);
         const size_t off = base + (size_t)tok * D + 4 * EPL * u + EPL * g;

@@ -440,9 +440,15 @@ def hardware_probes(torch, hla):
     mfma: 8 x 32x32x16 bf16 MFMAs per iteration and wave into four accumulators,
     one workgroup per CU with one or two waves per SIMD, for random bf16
     operands, all-zero operands, and one random register as both operands;
-    the shader clock is the workgroups' mean s_memtime cycles over the event
-    time. exp: 16 independent v_exp_f32 chains per thread, 512 threads per CU.
+    then with the A operands read from LDS (one 16-byte read per MFMA, as the
+    anchor reads K and V^T, or one per two MFMAs); the shader clock is the
+    workgroups' mean s_memtime cycles over the event time, and the matrix
+    cores' busy share is the rate over 2.5 PF scaled to that clock. exp: 16 independent v_exp_f32 chains per thread, 512 threads per CU.
     lds: ds_read_b128 of lane-consecutive chunks, 512 threads per CU.
+    hbm_stream: read two bf16 tensors and write a third with the gated linear
+    output pass's work split, once in its operand layout (every 16-byte access
+    of a wave touches 16 tokens x 64 bytes) and once in 1 KB consecutive runs
+    (and the two mixes), at the 480p and 720p shapes, two input sets alternating.
     hbm: torch copy (read 1 + write 1), add (read 2 + write 1) and fill
     (write) over 1 GiB bf16 tensors.
     """
@@ -487,6 +493,17 @@ def hardware_probes(torch, hla):
                          "ms": round(ms, 3), "TFLOP_s": round(tf, 1),
                          "frac_of_2500": round(tf / PEAK_BF16_TFLOPS, 3),
                          "shader_clock_GHz": round(cyc / (ms * 1e6), 3)})
+    lib.hla_probe_mfma_lds.argtypes = [I, I, I, I, P, P, P]
+    for r in (8, 4):
+        for w in (1, 2):
+            ms, cyc = timed(lambda: lib.hla_probe_mfma_lds(r, w, cus, iters, op, cp, st))
+            flops = 2.0 * 32 * 32 * 16 * 8 * iters * 4 * w * cus
+            tf = flops / (ms * 1e-3) / 1e12
+            ghz = cyc / (ms * 1e6)
+            rows.append({"probe": "mfma_f32_32x32x16_bf16", "operands": f"A from LDS, {r} reads per 8 MFMAs",
+                         "waves_per_simd": w, "ms": round(ms, 3), "TFLOP_s": round(tf, 1),
+                         "frac_of_2500": round(tf / PEAK_BF16_TFLOPS, 3), "shader_clock_GHz": round(ghz, 3),
+                         "matrix_core_busy": round(tf / (PEAK_BF16_TFLOPS * ghz / 2.4), 3)})
     ms, cyc = timed(lambda: lib.hla_probe_exp(cus, iters, op, cp, st))
     rows.append({"probe": "v_exp_f32", "ms": round(ms, 3),
                  "T_per_s": round(16.0 * iters * 512 * cus / (ms * 1e-3) / 1e12, 2),
@@ -497,6 +514,38 @@ def hardware_probes(torch, hla):
                  "bytes_per_CU_per_clock": round(8.0 * 16 * 512 * iters / cyc, 1),
                  "TB_s": round(8.0 * 16 * 512 * iters * cus / (ms * 1e-3) / 1e12, 1),
                  "shader_clock_GHz": round(cyc / (ms * 1e6), 3)})
+    # HBM streaming in the gated linear output pass's byte patterns (no arithmetic):
+    # two bf16 tensors read, one written, 16-token groups per wave, P = 512 / (B H)
+    lib.hla_probe_stream.argtypes = [I, I, I, I, P, P, P, P]
+    patterns = ("operand layout: 16 tokens x 64 B per access", "1 KB consecutive per access",
+                "1 KB loads, operand-layout stores", "operand-layout loads, 1 KB stores")
+    for N in (8190, 19320):
+        BH, D = 32, 128
+        sets = [[torch.randn(BH * N * D, device="cuda").to(torch.bfloat16) for _ in range(2)] for _ in range(2)]
+        o = torch.empty(BH * N * D, dtype=torch.bfloat16, device="cuda")
+        for mode, name in enumerate(patterns):
+            def launch(i):
+                q_, g_ = sets[i % 2]
+                return lib.hla_probe_stream(mode, 512 // BH, BH, N, P(q_.data_ptr()), P(g_.data_ptr()),
+                                            P(o.data_ptr()), st)
+            for i in range(2):
+                if launch(i) != 0:
+                    raise RuntimeError("probe launch failed")
+            torch.cuda.synchronize()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+            for i, (a, b) in enumerate(ev):
+                a.record()
+                launch(i)
+                b.record()
+            torch.cuda.synchronize()
+            ms = sorted(a.elapsed_time(b) for a, b in ev)[10]
+            row = {"probe": "hbm_stream", "pattern": name, "B*H": BH, "N": N, "D": D, "ms_median": round(ms, 4),
+                   "TB_s": round(3 * BH * N * D * 2 / (ms * 1e-3) / 1e12, 2)}
+            if mode < 2:  # o = q ^ g of the last call's set, in place
+                q_, g_ = sets[19 % 2]
+                row["exact"] = bool(torch.equal(o.view(torch.int16), q_.view(torch.int16) ^ g_.view(torch.int16)))
+            rows.append(row)
+        del sets, o
     n = 1 << 29  # 1 GiB of bf16
     x = torch.ones(n, dtype=torch.bfloat16, device="cuda")
     y = torch.ones_like(x)

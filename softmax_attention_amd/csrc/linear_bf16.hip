@@ -11,7 +11,8 @@
 //                   S^T rounded to bf16, z split into a bf16 hi + lo pair.
 //   3. output pass  per (b, h, token group): O = sigma(G) (.) (phi(Q) S) /
 //                   (phi(Q) . z + eps) with 16x16x32 bf16 MFMA, streaming Q and G
-//                   from HBM and writing O once.
+//                   from HBM and writing O once, each as whole 1 KB runs that a
+//                   per-wave LDS tile turns into (and back from) operand layout.
 // The operator is the O(N) fixed-size-state token mixer of SANA-Video 2.0
 // (ai-papers.net summary, section on hybrid linear attention; SANA-Video 2.0
 // abstract on thelatestinai.com).

@@ -194,6 +194,27 @@ def test_deterministic_and_in_bounds(op):
     assert torch.equal(outs[0], outs[1])
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, FP8])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("N", [1, 15, 17, 517])
+def test_linear_output_rows_stay_in_bounds(N, D, dtype):
+    """The output pass stores O in whole 1 KB runs of its 16-token groups; the
+    rows of a partial last group past N are computed but never stored. Guard
+    regions around `out` (NaN-filled) stay untouched, every element of `out` is
+    written, and the result matches the oracle, for bf16 and fp32 outputs."""
+    B, H = 1, 3
+    q, k, v, g = make((B, H, N, D), 5600 + N + D, dtype)
+    ref = oracle.gated_linear(q, k, v, g, 1e-6)
+    n, guard = B * H * N * D, 4096
+    for od in (torch.bfloat16, torch.float32):
+        buf = torch.full((n + 2 * guard,), float("nan"), dtype=od, device=DEV)
+        out = buf[guard:guard + n].view(B, H, N, D)
+        run_linear(q, k, v, g, out=out)
+        assert torch.isnan(buf[:guard]).all() and torch.isnan(buf[guard + n:]).all()
+        assert not torch.isnan(out).any()
+        assert rel_err(out, ref) <= TOL[torch.bfloat16]
+
+
 def test_empty_sequence_is_a_no_op():
     q = torch.empty((1, 2, 0, 128), dtype=torch.bfloat16, device=DEV)
     hla.hla_linear_fwd(q, q, q, q, out=torch.empty_like(q))

@@ -362,7 +362,8 @@ def main():
     if not args.no_stack:
         details["attnres_route"] = attnres_timing(torch, hla)
         details["stack"] = stack_timing(torch, hla)
-        details["other_workloads"] = [pair_timing(torch, hla, BY_NAME[n]) for n in ("480p_81f", "long_720p_193f")]
+        details["other_workloads"] = [pair_timing(torch, hla, BY_NAME[n], warmup=max(2, args.warmup))
+                                      for n in ("480p_81f", "long_720p_193f")]
         details["tiny_f32"] = tiny_timing(torch, hla)
         details["duration_sweep"] = duration_sweep(torch, hla, frames=(81, 121, 193, 481, 961), reps=1,
                                                    quiet=True)
@@ -703,12 +704,14 @@ def tiny_timing(torch, hla, reps: int = 50):
     return res
 
 
-def pair_timing(torch, hla, w, reps: int = 20, sm_reps: int = 6):
+def pair_timing(torch, hla, w, reps: int = 20, sm_reps: int = 6, warmup: int = 5):
     """One gated linear and one gated softmax layer of workload ``w`` (bf16).
 
     Two input sets alternate, so a call never finds its inputs in the 256 MB
     Infinity Cache from the previous call. Each call is timed by its own
-    events; the fractions use the mean, the median is reported beside it.
+    events after ``warmup`` untimed linear calls (as many as the benchmark step
+    takes; two for the longer softmax call); the fractions use the mean, the
+    median is reported beside it.
     """
     sets = [gpu_inputs(w, s_, torch) for s_ in range(2)]
     ws_l, ws_a = hla.linear_workspace(sets[0][0]), hla.anchor_workspace(sets[0][0])
@@ -717,8 +720,8 @@ def pair_timing(torch, hla, w, reps: int = 20, sm_reps: int = 6):
     for name, fn in (("linear", lambda i: hla.hla_linear_fwd(*sets[i % 2], out=out, eps=w.eps, workspace=ws_l)),
                      ("softmax", lambda i: hla.hla_softmax_anchor_fwd(*sets[i % 2], out=out, scale=w.scale,
                                                                       workspace=ws_a))):
-        fn(0)
-        fn(1)
+        for i in range(warmup if name == "linear" else 2):
+            fn(i)
         torch.cuda.synchronize()
         n = reps if name == "linear" else sm_reps
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]

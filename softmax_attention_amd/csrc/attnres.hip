@@ -12,7 +12,8 @@
 //   out_n = x_n + sum_i softmax_i(a)_i s_i,n
 // x, the summaries and out are fp32 [B, H, N, D] (the residual stream).
 //
-// One pass over HBM: each wave takes 16 tokens at a time; lane (n = lane & 15,
+// One pass over HBM: each wave takes 16 tokens at a time, moved as whole 1 KB
+// runs through a per-wave LDS tile; in registers lane (n = lane & 15,
 // g = lane >> 4) owns features 32t + 8g .. +7 (t < D/32) of token n. q comes
 // from 16x16x32 bf16 MFMAs with W^T fragments in LDS and x split into a bf16
 // hi + lo pair as the B operands (about 16 significant bits of x: the scores are
@@ -44,6 +45,18 @@ __device__ __forceinline__ u32x4 w_fragment(const uint16_t* __restrict__ W, int 
   return (u32x4){w[0], w[1], w[2], w[3]};
 }
 
+// 16-byte chunk c of token row t (R = D / 4 chunks per fp32 row, 16 or 32) in a
+// wave's staging tile: t R + (c ^ (t mod 16)), so the 16 lanes of one 16-byte LDS
+// access (16 consecutive chunks of a 1 KB run, or one chunk of 16 rows) land on 16
+// distinct bank groups.
+template <int R>
+__device__ __forceinline__ int run_slot(int t, int c) { return t * R + (c ^ (t & 15)); }
+
+// A wave's tile is written by some lanes and read by others; a wave's LDS
+// instructions execute in issue order, so keeping the compiler from moving them
+// across this point is all the ordering needed.
+__device__ __forceinline__ void wave_order() { asm volatile("" ::: "memory"); }
+
 // X may be out itself (in place): no __restrict__ on either.
 template <int D>
 __global__ __launch_bounds__(256, 2) void attnres_route(const float* X,
@@ -51,7 +64,10 @@ __global__ __launch_bounds__(256, 2) void attnres_route(const float* X,
                                                         const uint16_t* __restrict__ W,
                                                         float* out, int N) {
   constexpr int NT = D / 32, NJ = D / 16, NF = NJ * NT;
+  constexpr int R = D / 4;         // 16-byte chunks per fp32 token row
+  constexpr int NL = 16 * R / 64;  // 1 KB runs per 16-token group and tensor
   __shared__ u32x4 fr[NF * 64];
+  __shared__ f32x4 tile[4][16 * R];  // per wave: one tensor's group at a time
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int x = tid; x < NF * 64; x += 256) {
     const int f = x >> 6;
@@ -63,21 +79,40 @@ __global__ __launch_bounds__(256, 2) void attnres_route(const float* X,
   const size_t base = (size_t)bh * N * D;
   const float c = kLog2e * rsqrtf((float)D);  // scores in log2 units
   const int stride = gridDim.x * 4;
+  f32x4* const tl = tile[wave];
+  // Every tensor moves through HBM as whole 1 KB runs (lane l of run u: chunk
+  // 64u + l of the group's 16 rows), read once with the non-temporal cache
+  // policy; the tile turns them into the operand layout -- lane (n, g) takes
+  // chunks 8t + 2g and 8t + 2g + 1 of token n (features 32t + 8g .. +7) -- and the
+  // result back into runs. Rows past N read as zeros and are never stored.
   for (int grp = blockIdx.x * 4 + wave; grp * 16 < N; grp += stride) {
-    const int tok = grp * 16 + n;
-    const bool live = tok < N;
-    const size_t row = base + (size_t)(live ? tok : 0) * D + 8 * g;
-    // slice of a [B,H,N,D] fp32 tensor: features 32t + 8g + 0..7 of this token
-    auto load = [&](const float* T, f32x4* v) {
+    const size_t gbase = base + (size_t)grp * 16 * D;
+    auto load_runs = [&](const float* T, f32x4* raw) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        v[2 * t] = live ? *reinterpret_cast<const f32x4*>(T + row + 32 * t) : (f32x4){0.f, 0.f, 0.f, 0.f};
-        v[2 * t + 1] = live ? *reinterpret_cast<const f32x4*>(T + row + 32 * t + 4) : (f32x4){0.f, 0.f, 0.f, 0.f};
+      for (int u = 0; u < NL; ++u) {
+        const int k = 64 * u + lane;
+        raw[u] = grp * 16 + k / R < N ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(T + gbase + 4 * k))
+                                      : (f32x4){0.f, 0.f, 0.f, 0.f};
       }
     };
-    f32x4 xv[2 * NT], sv[2 * NT];
-    load(X, xv);
-    if (M > 0) load(S.p[0], sv);
+    auto stage = [&](const f32x4* raw, f32x4* v) {
+      wave_order();
+#pragma unroll
+      for (int u = 0; u < NL; ++u) {
+        const int k = 64 * u + lane;
+        tl[run_slot<R>(k / R, k % R)] = raw[u];
+      }
+      wave_order();
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        v[2 * t] = tl[run_slot<R>(n, 8 * t + 2 * g)];
+        v[2 * t + 1] = tl[run_slot<R>(n, 8 * t + 2 * g + 1)];
+      }
+    };
+    f32x4 raw[NL], sraw[NL], xv[2 * NT];
+    load_runs(X, raw);
+    if (M > 0) load_runs(S.p[0], sraw);
+    stage(raw, xv);
 
     // q = x W on the matrix cores. The fragments are re-read from LDS every
     // group: an opaque (always equal) offset keeps the compiler from hoisting all
@@ -118,9 +153,8 @@ __global__ __launch_bounds__(256, 2) void attnres_route(const float* X,
     for (int x = 0; x < 2 * NT; ++x) r[x] = (f32x4){0.f, 0.f, 0.f, 0.f};
     for (int i = 0; i < M; ++i) {
       f32x4 cur[2 * NT];
-#pragma unroll
-      for (int x = 0; x < 2 * NT; ++x) cur[x] = sv[x];
-      if (i + 1 < M) load(S.p[i + 1], sv);  // next block in flight
+      stage(sraw, cur);
+      if (i + 1 < M) load_runs(S.p[i + 1], sraw);  // next block in flight
       float part = 0.f;
 #pragma unroll
       for (int x = 0; x < 2 * NT; ++x)
@@ -140,12 +174,19 @@ __global__ __launch_bounds__(256, 2) void attnres_route(const float* X,
       for (int x = 0; x < 2 * NT; ++x) r[x] = r[x] * corr + p * cur[x];
       m = m_new;
     }
-    if (!live) continue;
     const float inv = M > 0 ? 1.0f / l : 0.f;
+    wave_order();
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      *reinterpret_cast<f32x4*>(out + row + 32 * t) = xv[2 * t] + r[2 * t] * inv;
-      *reinterpret_cast<f32x4*>(out + row + 32 * t + 4) = xv[2 * t + 1] + r[2 * t + 1] * inv;
+      tl[run_slot<R>(n, 8 * t + 2 * g)] = xv[2 * t] + r[2 * t] * inv;
+      tl[run_slot<R>(n, 8 * t + 2 * g + 1)] = xv[2 * t + 1] + r[2 * t + 1] * inv;
+    }
+    wave_order();
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int k = 64 * u + lane;
+      const f32x4 o = tl[run_slot<R>(k / R, k % R)];
+      if (grp * 16 + k / R < N) *reinterpret_cast<f32x4*>(out + gbase + 4 * k) = o;
     }
   }
 }

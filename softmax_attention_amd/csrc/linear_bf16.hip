@@ -502,16 +502,21 @@ __global__ __launch_bounds__(256) void linear_reduce_bf16(const char* __restrict
 // holds 16 bytes of Q and of G of token n per run, features 32u + 8g .. +7
 // (bf16) or 64u + 16g .. +15 (fp8, two k-steps). That is both its B-operand
 // slice and, by the fragment order (frag_pos), the feature run of its output
-// values. A bf16 O goes back through the same tile and leaves as 1 KB runs too;
-// an fp32 O, or one added into, is stored from the operand layout (16-byte
-// accesses, 64 bytes per token and instruction).
+// values. O goes back through the same tile and leaves as 1 KB runs too (an
+// fp32 O added into the stream at those runs); only a bf16 O added into is
+// stored from the operand layout (16-byte accesses, 64 bytes per token and
+// instruction), so that each sum is rounded to bf16 once, as before.
 //
 // Tile slots are 16-byte chunks: chunk c of token row t (R chunks per row) sits
-// at t R + (c ^ ((t / (16 / R)) mod R)), so the 16 lanes of one 16-byte LDS
+// at t R + (c ^ ((t / (16 / R)) mod R)) for R <= 16 and at t R + (c ^ (t mod 16))
+// for wider rows (an fp32 O), so the 16 lanes of one 16-byte LDS
 // access (16 consecutive chunks of the 1 KB run, or one chunk of 16 rows) land
 // on 16 distinct bank groups.
 template <int R>
-__device__ __forceinline__ int out_slot(int t, int c) { return t * R + (c ^ ((t / (16 / R)) & (R - 1))); }
+__device__ __forceinline__ int out_slot(int t, int c) {
+  if constexpr (R >= 16) return t * R + (c ^ (t & 15));
+  else return t * R + (c ^ ((t / (16 / R)) & (R - 1)));
+}
 
 // A wave's LDS tile is written by some lanes and read by others; a wave's LDS
 // instructions execute in issue order, so keeping the compiler from moving
@@ -532,9 +537,11 @@ __global__ __launch_bounds__(256, 2) void linear_out_bf16(const TIn* __restrict_
   constexpr int CPR = D * (int)sizeof(TIn) / 16;  // 16-byte chunks per token row of Q or G
   constexpr int OCPR = D / 8;                     // 16-byte chunks per token row of a bf16 O
   constexpr int TILE = 16 * CPR;                  // chunks of Q (or G) per group
+  constexpr int FCPR = D / 4;                     // 16-byte chunks per token row of an fp32 O
+  constexpr int XS = OUT_F32 && 16 * FCPR > 2 * TILE ? 16 * FCPR : 2 * TILE;
   static_assert(CPR == 4 * NU && 16 * OCPR <= 2 * TILE, "tile shapes");
   __shared__ u32x4 fr[NF * 64];
-  __shared__ u32x4 xs[4][2 * TILE];  // per wave: Q and G of its group, then its bf16 O
+  __shared__ u32x4 xs[4][XS];  // per wave: Q and G of its group, then its O
   // fp8 gates take 256 values: sigma of each, computed once per workgroup with
   // the same sigmoid, replaces an exp and a reciprocal per output element
   __shared__ float sig_tab[F8 ? 256 : 1];
@@ -670,7 +677,38 @@ __global__ __launch_bounds__(256, 2) void linear_out_bf16(const TIn* __restrict_
         const u32x4 ov = tq[out_slot<OCPR>(t, k % OCPR)];
         if (gi * 16 + t < N) stg16(dst + 8 * k, ov);
       }
+    } else if (OUT_F32) {
+      // fp32 O through the tile the same way; added into the stream at the
+      // run positions when accumulating
+      wave_lds_order();
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        float o[EPL], sg[EPL];
+#pragma unroll
+        for (int jj = 0; jj < JPU; ++jj)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[4 * jj + e] = acc[JPU * u + jj][e];
+        gate_values(gv[u], sg);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[e] = sg[e] * (o[e] * rden);
+#pragma unroll
+        for (int x = 0; x < EPL / 4; ++x)
+          tq[out_slot<FCPR>(n, (4 * u + g) * (EPL / 4) + x)] = __builtin_bit_cast(
+              u32x4, (f32x4){o[4 * x], o[4 * x + 1], o[4 * x + 2], o[4 * x + 3]});
+      }
+      wave_lds_order();
+      float* dst = reinterpret_cast<float*>(out) + base + (size_t)gi * 16 * D;
+#pragma unroll
+      for (int v = 0; v < FCPR / 4; ++v) {
+        const int k = 64 * v + lane, t = k / FCPR;
+        f32x4 ov = __builtin_bit_cast(f32x4, tq[out_slot<FCPR>(t, k % FCPR)]);
+        if (gi * 16 + t < N) {
+          if (accumulate) ov += *reinterpret_cast<const f32x4*>(dst + 4 * k);
+          *reinterpret_cast<f32x4*>(dst + 4 * k) = ov;
+        }
+      }
     } else if (tok < N) {
+      // a bf16 O added into: from the operand layout, each run's sum rounded once
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
         // run u: fragments JPU*u .. +JPU-1, 4 consecutive features each
@@ -682,31 +720,18 @@ __global__ __launch_bounds__(256, 2) void linear_out_bf16(const TIn* __restrict_
         gate_values(gv[u], sg);
 #pragma unroll
         for (int e = 0; e < EPL; ++e) o[e] = sg[e] * (o[e] * rden);
-        const size_t off = base + (size_t)tok * D + 4 * EPL * u + EPL * g;
-        if (OUT_F32) {
-          float* dst = reinterpret_cast<float*>(out) + off;
+        uint16_t* dst = reinterpret_cast<uint16_t*>(out) + base + (size_t)tok * D + 4 * EPL * u + EPL * g;
 #pragma unroll
-          for (int x = 0; x < EPL / 4; ++x) {
-            f32x4 v = (f32x4){o[4 * x], o[4 * x + 1], o[4 * x + 2], o[4 * x + 3]};
-            if (accumulate) v += *reinterpret_cast<const f32x4*>(dst + 4 * x);
-            *reinterpret_cast<f32x4*>(dst + 4 * x) = v;
+        for (int x = 0; x < EPL / 8; ++x) {
+          const u32x4 prev = ldg16(dst + 8 * x);
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            o[8 * x + 2 * p] += bf_lo(prev[p]);
+            o[8 * x + 2 * p + 1] += bf_hi(prev[p]);
           }
-        } else {
-          uint16_t* dst = reinterpret_cast<uint16_t*>(out) + off;
-#pragma unroll
-          for (int x = 0; x < EPL / 8; ++x) {
-            if (accumulate) {
-              const u32x4 prev = ldg16(dst + 8 * x);
-#pragma unroll
-              for (int p = 0; p < 4; ++p) {
-                o[8 * x + 2 * p] += bf_lo(prev[p]);
-                o[8 * x + 2 * p + 1] += bf_hi(prev[p]);
-              }
-            }
-            stg16(dst + 8 * x, (u32x4){pack_bf16(o[8 * x], o[8 * x + 1]), pack_bf16(o[8 * x + 2], o[8 * x + 3]),
-                                       pack_bf16(o[8 * x + 4], o[8 * x + 5]),
-                                       pack_bf16(o[8 * x + 6], o[8 * x + 7])});
-          }
+          stg16(dst + 8 * x, (u32x4){pack_bf16(o[8 * x], o[8 * x + 1]), pack_bf16(o[8 * x + 2], o[8 * x + 3]),
+                                     pack_bf16(o[8 * x + 4], o[8 * x + 5]),
+                                     pack_bf16(o[8 * x + 6], o[8 * x + 7])});
         }
       }
     }

@@ -201,7 +201,8 @@ def test_linear_output_rows_stay_in_bounds(N, D, dtype):
     """The output pass stores O in whole 1 KB runs of its 16-token groups; the
     rows of a partial last group past N are computed but never stored. Guard
     regions around `out` (NaN-filled) stay untouched, every element of `out` is
-    written, and the result matches the oracle, for bf16 and fp32 outputs."""
+    written, and the result matches the oracle, for bf16 and fp32 outputs and
+    for an fp32 stream the output is added into."""
     B, H = 1, 3
     q, k, v, g = make((B, H, N, D), 5600 + N + D, dtype)
     ref = oracle.gated_linear(q, k, v, g, 1e-6)
@@ -213,6 +214,15 @@ def test_linear_output_rows_stay_in_bounds(N, D, dtype):
         assert torch.isnan(buf[:guard]).all() and torch.isnan(buf[guard + n:]).all()
         assert not torch.isnan(out).any()
         assert rel_err(out, ref) <= TOL[torch.bfloat16]
+    # accumulating into an fp32 stream: the previous values are read at the same
+    # runs, so the guards stay NaN and every element is x0 + O
+    x0 = custom((B, H, N, D), 5650 + N, torch.float32, n=1)[0]
+    buf = torch.full((n + 2 * guard,), float("nan"), dtype=torch.float32, device=DEV)
+    x = buf[guard:guard + n].view(B, H, N, D)
+    x.copy_(x0.to(DEV))
+    run_linear(q, k, v, g, out=x, accumulate=True)
+    assert torch.isnan(buf[:guard]).all() and torch.isnan(buf[guard + n:]).all()
+    assert rel_err(x.cpu() - x0, ref) <= TOL[torch.bfloat16]
 
 
 def test_empty_sequence_is_a_no_op():
